@@ -1,0 +1,193 @@
+"""CPU oracle for MoE dispatch / combine -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library and its Python binding
+never do; the two share no code.
+
+This wrapper only marshals numpy arrays into ``liboracle.so`` (built from
+``oracle.c`` with gcc, ``-O2 -ffp-contract=off``); the arithmetic is in C.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle.so (always recompiles)."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        L.oracle_bf16_rne.argtypes = [ctypes.c_float]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_e4m3fn_rne_sat.argtypes = [ctypes.c_float]
+        L.oracle_e4m3fn_rne_sat.restype = ctypes.c_uint8
+        L.oracle_e4m3fn_to_f32.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3fn_to_f32.restype = ctypes.c_float
+        L.oracle_e4m3fn_encode_array.argtypes = [P, P, ctypes.c_int64]
+        L.oracle_e4m3fn_encode_array.restype = None
+        L.oracle_quant_block.argtypes = [P, P, P]
+        L.oracle_quant_block.restype = None
+        L.oracle_layout.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
+        L.oracle_layout.restype = i32
+        L.oracle_expert_offsets.argtypes = [P, i32, P]
+        L.oracle_expert_offsets.restype = None
+        L.oracle_slots.argtypes = [P, P, i32, i32, P, i32, i32, P, P, P]
+        L.oracle_slots.restype = None
+        L.oracle_dispatch.argtypes = [P, i32, i32, i32, P, i32, P, P]
+        L.oracle_dispatch.restype = None
+        L.oracle_combine.argtypes = [P, i32, i32, i32, P, P, P]
+        L.oracle_combine.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# -- codec -------------------------------------------------------------------
+
+def bf16_rne(f: float) -> int:
+    return int(lib().oracle_bf16_rne(float(f)))
+
+
+def e4m3fn(v: float) -> int:
+    return int(lib().oracle_e4m3fn_rne_sat(float(v)))
+
+
+def e4m3fn_array(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32)
+    q = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_e4m3fn_encode_array(_p(v), _p(q), v.size)
+    return q
+
+
+def e4m3fn_decode(q: int) -> float:
+    return float(lib().oracle_e4m3fn_to_f32(int(q)))
+
+
+def quant_block(x128_bits: np.ndarray):
+    x = _c(x128_bits, np.uint16)
+    assert x.size == 128
+    q = np.empty(128, dtype=np.uint8)
+    s = np.empty(1, dtype=np.float32)
+    lib().oracle_quant_block(_p(x), _p(q), _p(s))
+    return q, np.float32(s[0])
+
+
+# -- the path ----------------------------------------------------------------
+
+def layout(topk_idx: np.ndarray, E: int, P: int):
+    """Returns dict(num_tokens_per_expert, num_tokens_per_partition,
+    is_token_in_partition [T,P] uint8, num_invalid int, valid [T,K] uint8)."""
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    cnt = np.empty(E, np.int32)
+    pc = np.empty(P, np.int32)
+    mask = np.empty((T, P), np.uint8)
+    ninv = np.empty(1, np.int32)
+    valid = np.empty((T, K), np.uint8)
+    rc = lib().oracle_layout(_p(idx), T, K, E, P, _p(cnt), _p(pc), _p(mask), _p(ninv), _p(valid))
+    if rc != 0:
+        raise ValueError("oracle_layout: invalid dimensions")
+    return dict(num_tokens_per_expert=cnt, num_tokens_per_partition=pc,
+                is_token_in_partition=mask, num_invalid=int(ninv[0]), valid=valid)
+
+
+def expert_offsets(cnt: np.ndarray) -> np.ndarray:
+    cnt = _c(cnt, np.int32)
+    off = np.empty(cnt.size + 1, np.int32)
+    lib().oracle_expert_offsets(_p(cnt), cnt.size, _p(off))
+    return off
+
+
+def slots(topk_idx: np.ndarray, valid: np.ndarray, off: np.ndarray, capacity: int):
+    """Returns (slot [T,K] int32, src_token [capacity] int32 (-1 where unset), overflow int)."""
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    valid = _c(valid, np.uint8)
+    off = _c(off, np.int32)
+    E = off.size - 1
+    slot = np.empty((T, K), np.int32)
+    src = np.full(max(capacity, 1), -1, np.int32)
+    ovf = np.zeros(1, np.int32)
+    lib().oracle_slots(_p(idx), _p(valid), T, K, _p(off), E, capacity, _p(slot), _p(src), _p(ovf))
+    return slot, src[:capacity], int(ovf[0])
+
+
+def dispatch(x_bits: np.ndarray, slot: np.ndarray, rows: int, use_fp8: bool):
+    """Returns (recv [rows,H] uint8|uint16, scales [rows,H/128] fp32 or None).
+    Rows that no pair maps to are left zero."""
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    slot = _c(slot, np.int32)
+    K = slot.shape[1]
+    if use_fp8:
+        recv = np.zeros((rows, H), np.uint8)
+        scales = np.zeros((rows, H // 128), np.float32)
+        lib().oracle_dispatch(_p(x), T, H, K, _p(slot), 1, _p(recv), _p(scales))
+        return recv, scales
+    recv = np.zeros((rows, H), np.uint16)
+    lib().oracle_dispatch(_p(x), T, H, K, _p(slot), 0, _p(recv), None)
+    return recv, None
+
+
+def combine(y_bits: np.ndarray, slot: np.ndarray, w: np.ndarray) -> np.ndarray:
+    y = _c(y_bits, np.uint16)
+    slot = _c(slot, np.int32)
+    w = _c(w, np.float32)
+    T, K = slot.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().oracle_combine(_p(y), T, H, K, _p(slot), _p(w), _p(out))
+    return out
+
+
+def run_all(topk_idx, topk_weights, x_bits, E, P, use_fp8, capacity=None, y_bits=None):
+    """The whole path on the CPU: layout, offsets, slots, dispatch and, when
+    y_bits is given, combine.  Returns a dict of every intermediate."""
+    T, K = topk_idx.shape
+    lay = layout(topk_idx, E, P)
+    off = expert_offsets(lay["num_tokens_per_expert"])
+    cap = T * K if capacity is None else capacity
+    slot, src, ovf = slots(topk_idx, lay["valid"], off, cap)
+    N = int(off[-1])
+    rows = min(N, cap)
+    res = dict(lay, expert_offset=off, slot=slot, src_token=src[:rows], overflow=ovf, N=N, rows=rows)
+    if x_bits is not None:
+        recv, scales = dispatch(x_bits, slot, rows, use_fp8)
+        res.update(recv_x=recv, recv_scales=scales)
+    if y_bits is not None:
+        res["out"] = combine(y_bits, slot, topk_weights)
+    return res

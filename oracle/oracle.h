@@ -1,0 +1,80 @@
+/*
+ * CPU oracle for MoE dispatch / combine -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load or call this library.  The GPU library never does, and
+ * shares no code with it.
+ *
+ * It is the plain, slow definition of what the hot path computes, written from
+ * the DeepEP pages:
+ *   - the call flow get_dispatch_layout -> dispatch(x, topk_idx, topk_weights)
+ *     -> expert GEMM -> combine(y, handle), and "backward of dispatch is
+ *     combine and vice versa" (stakiran github-trend-summarizer, DeepEP 要約,
+ *     section 3 "使うときの流れ");
+ *   - the handle carries the routing metadata combine needs, and
+ *     handle.num_recv_tokens_per_expert_list gives per-expert counts for the
+ *     GEMM (GeekNews, "Mẫu sử dụng cho huấn luyện, prefill và decoding");
+ *   - FP8 dispatch with BF16 combine (aikraft.ru, "Технические детали и
+ *     требования"; GeekNews, "Kết quả đo hiệu năng");
+ *   - reuse of routing metadata through a cached handle (GeekNews, same usage
+ *     section).
+ * Where the pages leave a step open (receive layout, id validity rules, FP8
+ * variant and scale convention, combine summation order) the readings are the
+ * ones stated beside each function below.
+ *
+ * Every function is single-threaded plain loops.  Build with -O2
+ * -ffp-contract=off so that every fp32 operation is the single IEEE operation
+ * the source names (fmaf is an explicit fused multiply-add).
+ */
+#ifndef MOE_EP_ORACLE_H
+#define MOE_EP_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Codec helpers (exported so that tests can pin them one value at a time). */
+uint16_t oracle_bf16_rne(float f);         /* fp32 -> bf16, round to nearest even   */
+float    oracle_bf16_to_f32(uint16_t b);   /* exact widening                         */
+uint8_t  oracle_e4m3fn_rne_sat(float v);   /* fp32 -> OCP E4M3FN, RNE, satfinite     */
+float    oracle_e4m3fn_to_f32(uint8_t q);  /* exact decode (0x7F/0xFF -> NaN)        */
+void     oracle_e4m3fn_encode_array(const float* v, uint8_t* q, int64_t n);
+
+/* Quantise one block of 128 BF16 values: q[128] codes and the scale s. */
+void oracle_quant_block(const uint16_t* x128, uint8_t* q128, float* scale);
+
+/* Step 1, layout.  valid[T*K] receives 1 for a pair that takes part in
+ * dispatch, 0 for masked (id < 0), out-of-range (id >= E) or repeated ids.
+ * Returns 0, or -1 on invalid dimensions. */
+int oracle_layout(const int64_t* topk_idx, int T, int K, int E, int P,
+                  int32_t* num_tokens_per_expert, int32_t* num_tokens_per_partition,
+                  uint8_t* is_token_in_partition, int32_t* num_invalid,
+                  uint8_t* valid);
+
+/* Exclusive prefix sum of per-expert counts: off[0] = 0, off[E] = N. */
+void oracle_expert_offsets(const int32_t* num_tokens_per_expert, int E, int32_t* off);
+
+/* Step 2, slots.  slot[T*K] (-1 when not dispatched), src_token[capacity]
+ * (entries at and beyond min(N, capacity) are left untouched), *overflow = 1
+ * when a pair's slot would be >= capacity. */
+void oracle_slots(const int64_t* topk_idx, const uint8_t* valid, int T, int K,
+                  const int32_t* off, int E, int capacity,
+                  int32_t* slot, int32_t* src_token, int32_t* overflow);
+
+/* Step 3, permute (BF16: bit copy of the row) or quantise-then-permute (FP8).
+ * recv has capacity rows of H elements (uint16 bf16 or uint8 e4m3fn);
+ * scales has capacity rows of H/128 fp32 (FP8 mode only). */
+void oracle_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* slot,
+                     int use_fp8, void* recv, float* scales);
+
+/* Combine: out[t, j] = bf16_rne( fmaf chain over k ascending of
+ * w[t,k] * y[slot[t,k], j], starting from +0.0f, skipping slot < 0 ). */
+void oracle_combine(const uint16_t* y, int T, int H, int K, const int32_t* slot,
+                    const float* w, uint16_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

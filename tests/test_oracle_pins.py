@@ -1,0 +1,479 @@
+"""Pins for the CPU oracle: every check compares it with something other than
+itself -- torch's CPU codecs, brute-force search, a textbook stable sort,
+numpy bincount / unique, hand-worked values, exact identities and error
+bounds that hold for the mathematics."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(bits_u16):
+    return workloads.f32_from_bf16_bits(bits_u16)
+
+
+# ----------------------------------------------------------------------------
+# BF16 rounding
+# ----------------------------------------------------------------------------
+
+def test_bf16_rne_matches_torch_on_random_and_ties():
+    rng = np.random.default_rng(11)
+    u = rng.integers(0, 1 << 32, 200000, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]                       # finite only
+    ties = (rng.integers(0, 1 << 16, 20000, dtype=np.uint32) << 16) | 0x8000
+    ties = ties[((ties >> 23) & 0xFF) < 0xFE]                # stay clear of overflow
+    near = np.concatenate([ties - 1, ties + 1])
+    for arr in (u, ties.astype(np.uint32), near.astype(np.uint32)):
+        f = arr.view(np.float32)
+        ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        got = np.array([oracle.bf16_rne(v) for v in f[:5000]], dtype=np.uint16)
+        assert np.array_equal(got, ref[:5000])
+
+
+def test_bf16_widening_is_exact():
+    for b in [0x0000, 0x8000, 0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x4049]:
+        assert np.float32(oracle.lib().oracle_bf16_to_f32(b)) == _f32(np.array([b], np.uint16))[0]
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3FN codec
+# ----------------------------------------------------------------------------
+
+def _e4m3_table():
+    """All 127 non-negative finite E4M3FN values, built from the bit layout."""
+    vals, codes = [], []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        vals.append(v)
+        codes.append(code)
+    return np.array(vals), np.array(codes)
+
+
+def _nearest_brute(v):
+    """Nearest E4M3FN value by exhaustive search; ties to the even code;
+    saturate at 448; keep the sign."""
+    tv, tc = _e4m3_table()
+    a = np.abs(v.astype(np.float64))
+    d = np.abs(a[:, None] - tv[None, :])
+    dmin = d.min(axis=1, keepdims=True)
+    cand = d == dmin
+    # among tied candidates prefer an even code
+    even = cand & ((tc[None, :] & 1) == 0)
+    pick = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+    code = tc[pick].astype(np.uint8)
+    code[a >= 448.0] = 0x7E
+    return code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+
+
+def test_e4m3fn_hand_values():
+    g = json.load(open(os.path.join(GOLDEN, "e4m3fn_values.json")))
+    for v, code in g["cases"]:
+        assert oracle.e4m3fn(np.float32(v)) == int(code, 16), (v, code)
+
+
+def test_e4m3fn_matches_brute_force_nearest():
+    rng = np.random.default_rng(5)
+    tv, _ = _e4m3_table()
+    mids = (tv[1:] + tv[:-1]) / 2
+    pts = np.concatenate([tv, mids]).astype(np.float32)
+    # every value and midpoint, and the fp32 neighbours of each
+    u = pts.view(np.uint32)
+    around = np.concatenate([u, u + 1, np.maximum(u, 1) - 1]).view(np.float32)
+    rnd = (rng.random(60000) * 500).astype(np.float32)
+    tiny = (rng.random(20000) * 2 ** -5).astype(np.float32)
+    v = np.concatenate([around, rnd, tiny, [464.0, 480.0, 1e30]]).astype(np.float32)
+    v = np.concatenate([v, -v])
+    assert np.array_equal(oracle.e4m3fn_array(v), _nearest_brute(v))
+
+
+@pytest.mark.slow
+def test_e4m3fn_exhaustive_against_torch():
+    """Every fp32 bit pattern in [2^-11, 448] and its negative: the oracle's
+    encoder equals torch's CPU float8_e4m3fn conversion (RNE, same format).
+    Below 2^-11 both give signed zero (checked on a sample)."""
+    lo = np.float32(2.0 ** -11).view(np.uint32)
+    hi = np.float32(448.0).view(np.uint32)
+    step = 1 << 24
+    for start in range(int(lo), int(hi) + 1, step):
+        u = np.arange(start, min(start + step, int(hi) + 1), dtype=np.uint32)
+        for sign in (0, 0x80000000):
+            v = (u | np.uint32(sign)).view(np.float32)
+            ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            got = oracle.e4m3fn_array(v)
+            bad = np.nonzero(got != ref)[0]
+            assert bad.size == 0, (v[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    rng = np.random.default_rng(3)
+    small = rng.integers(0, int(lo), 1 << 20, dtype=np.uint64).astype(np.uint32)
+    v = np.concatenate([small, small | np.uint32(0x80000000)]).view(np.float32)
+    assert np.array_equal(oracle.e4m3fn_array(v), torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_e4m3fn_decode_roundtrip_and_bound():
+    for code in range(256):
+        if code & 0x7F == 0x7F:
+            assert np.isnan(oracle.e4m3fn_decode(code))
+            continue
+        v = oracle.e4m3fn_decode(code)
+        assert oracle.e4m3fn(v) == code
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal(20000) * 40).astype(np.float32)
+    v = v[np.abs(v) < 448]
+    q = oracle.e4m3fn_array(v)
+    dec = np.array([oracle.e4m3fn_decode(c) for c in q])
+    a = np.abs(v.astype(np.float64))
+    # half a quantum: 2^-4 relative in the normal range, 2^-10 absolute below 2^-6
+    bound = np.where(a >= 2 ** -6, a * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(dec - v) <= bound)
+
+
+# ----------------------------------------------------------------------------
+# block quantisation
+# ----------------------------------------------------------------------------
+
+def _blocks(seed, kind, n=64):
+    return workloads.random_rows(seed, n, 128, kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "wide", "bits", "ties"])
+def test_quant_block_properties(kind):
+    for row in _blocks(21, kind):
+        q, s = oracle.quant_block(row)
+        v = _f32(row).astype(np.float64)
+        amax = np.abs(v).max()
+        a = max(amax, 2.0 ** -64)
+        # scale is the closed form a / 448 rounded to fp32 (exact quotient
+        # within half an fp32 ulp)
+        assert abs(float(s) - a / 448.0) <= 2.0 ** -24 * (a / 448.0)
+        # the element(s) equal to amax map to +-448 exactly
+        if amax > 0:
+            for i in np.nonzero(np.abs(v) == amax)[0]:
+                assert q[i] & 0x7F == 0x7E
+        dec = np.array([oracle.e4m3fn_decode(c) for c in q]) * float(s)
+        # dequantisation error: half an E4M3 quantum of v * inv, with slack
+        # 2^-20 for the fp32 roundings of inv, s and the product
+        vin = np.abs(v) * (448.0 / a)
+        bound = np.where(vin >= 2 ** -6, 2.0 ** -4 * np.abs(v), 2.0 ** -10 * float(s)) * (1 + 2.0 ** -20)
+        assert np.all(np.abs(dec - v) <= bound + 1e-300)
+        # sign kept, including zero
+        assert np.all((q >> 7) == np.signbit(v).astype(np.uint8))
+        # monotone: ordering of values is kept (weakly) by the codes
+        order = np.argsort(v, kind="stable")
+        dq = np.array([oracle.e4m3fn_decode(c) for c in q])[order]
+        assert np.all(np.diff(dq) >= 0)
+
+
+def test_quant_block_special_cases():
+    z = workloads.bf16_bits_from_f32(np.zeros(128, np.float32))
+    z[3] = 0x8000  # -0
+    q, s = oracle.quant_block(z)
+    assert float(s) == np.float32(2.0 ** -64) / np.float32(448.0)
+    assert q[3] == 0x80 and np.all(np.delete(q, 3) == 0)
+    one = np.zeros(128, np.float32)
+    one[77] = -3.0
+    q, s = oracle.quant_block(workloads.bf16_bits_from_f32(one))
+    assert q[77] == 0xFE and np.all(np.delete(q, 77) == 0)
+    assert float(s) == np.float32(3.0) / np.float32(448.0)
+    # amax 224 -> inv 2 exactly, scale 0.5 exactly
+    b = np.zeros(128, np.float32)
+    b[0], b[1], b[2], b[3] = 224.0, 1.0, 0.001, -0.0029296875
+    q, s = oracle.quant_block(workloads.bf16_bits_from_f32(b))
+    assert float(s) == 0.5
+    assert q[0] == 0x7E and q[1] == 0x40
+    # 0.001 in bf16 is 0.00099945068..., times 2 -> 1.0*2^-9 nearest -> 0x01
+    assert q[2] == 0x01
+    # -0.0029296875 * 2 = -3 * 2^-9 -> 0x83
+    assert q[3] == 0x83
+    # bf16 subnormal inputs: a = 2^-64 and every code is a signed zero
+    sub = workloads.random_rows(4, 1, 128, "subnormal")[0]
+    q, s = oracle.quant_block(sub)
+    assert np.all(q & 0x7F == 0)
+
+
+# ----------------------------------------------------------------------------
+# layout / offsets / slots
+# ----------------------------------------------------------------------------
+
+def _valid_independent(idx, E):
+    """First valid occurrence of each in-range id per row, via np.unique."""
+    T, K = idx.shape
+    v = np.zeros((T, K), np.uint8)
+    for t in range(T):
+        row = idx[t]
+        ok = np.nonzero((row >= 0) & (row < E))[0]
+        if ok.size:
+            _, first = np.unique(row[ok], return_index=True)
+            v[t, ok[first]] = 1
+    return v
+
+
+def test_layout_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "layout_worked_example.json")))
+    idx = np.array(g["topk_idx"], np.int64)
+    lay = oracle.layout(idx, g["E"], g["P"])
+    assert lay["num_tokens_per_expert"].tolist() == g["num_tokens_per_expert"]
+    assert lay["num_tokens_per_partition"].tolist() == g["num_tokens_per_partition"]
+    assert lay["is_token_in_partition"].tolist() == g["is_token_in_partition"]
+    assert lay["num_invalid"] == g["num_invalid"]
+    off = oracle.expert_offsets(lay["num_tokens_per_expert"])
+    assert off.tolist() == g["expert_offset"]
+    slot, src, ovf = oracle.slots(idx, lay["valid"], off, 15)
+    assert slot.tolist() == g["slot"] and ovf == 0
+    assert src[:off[-1]].tolist() == g["src_token"]
+    c6 = g["capacity_6"]
+    slot6, src6, ovf6 = oracle.slots(idx, lay["valid"], off, 6)
+    assert slot6.tolist() == c6["slot"] and src6.tolist() == c6["src_token"] and ovf6 == c6["overflow"]
+    cb = g["combine"]
+    y = np.array([[r, -r] for r in range(9)], np.float32)
+    out = oracle.combine(workloads.bf16_bits_from_f32(y), slot, np.array(cb["weights"], np.float32))
+    assert np.array_equal(_f32(out), np.array(cb["out"], np.float32))
+
+
+CASES = [
+    dict(T=1, E=1, K=1, P=1), dict(T=7, E=8, K=3, P=2), dict(T=64, E=16, K=4, P=4),
+    dict(T=65, E=32, K=8, P=8), dict(T=300, E=64, K=6, P=8), dict(T=513, E=256, K=8, P=16),
+    dict(T=200, E=1024, K=16, P=64), dict(T=50, E=5, K=5, P=5),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("mode", ["clean", "masked", "dirty"])
+def test_layout_and_slots_against_independent_definitions(case, mode):
+    T, E, K, P = case["T"], case["E"], case["K"], case["P"]
+    kw = dict(clean={}, masked=dict(mask_frac=0.2),
+              dirty=dict(distinct=False, mask_frac=0.1, invalid_frac=0.1, dup_frac=0.2))[mode]
+    idx, w = workloads.random_case(1000 + T, T, E, K, **kw)
+    lay = oracle.layout(idx, E, P)
+    valid = _valid_independent(idx, E)
+    assert np.array_equal(lay["valid"], valid)
+    masked = int((idx < 0).sum())
+    ninv = T * K - masked - int(valid.sum())
+    assert lay["num_invalid"] == ninv
+    cnt = np.bincount(idx[valid == 1], minlength=E)
+    assert np.array_equal(lay["num_tokens_per_expert"], cnt)
+    assert cnt.sum() == T * K - masked - ninv
+    epp = E // P
+    part = np.zeros((T, P), np.uint8)
+    for t in range(T):
+        for e in np.unique(idx[t][valid[t] == 1]):
+            part[t, e // epp] = 1
+    assert np.array_equal(lay["is_token_in_partition"], part)
+    pc = lay["num_tokens_per_partition"]
+    assert np.array_equal(pc, part.sum(axis=0))
+    assert np.all(pc <= T)
+    for p in range(P):
+        assert pc[p] >= cnt[p * epp:(p + 1) * epp].max(initial=0)
+    off = oracle.expert_offsets(cnt)
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(cnt)]))
+    N = int(off[-1])
+    for cap in (T * K, N, max(N - 7, 0), N // 2, 0):
+        slot, src, ovf = oracle.slots(idx, lay["valid"], off, cap)
+        # textbook stable sort of the flattened pairs by expert id; invalid
+        # pairs sort last
+        key = np.where(valid.reshape(-1) == 1, idx.reshape(-1), np.int64(1) << 62)
+        order = np.argsort(key, kind="stable")
+        rank = np.empty(order.size, np.int64)
+        rank[order] = np.arange(order.size)
+        exp = np.where((valid.reshape(-1) == 1) & (rank < cap), rank, -1).reshape(T, K)
+        assert np.array_equal(slot, exp)
+        assert ovf == int(N > cap)
+        rows = min(N, cap)
+        tok = np.repeat(np.arange(T), K)
+        assert np.array_equal(src[:rows], tok[order[:rows]])
+        if cap >= N:
+            # bijection onto [0, N), each row inside its expert's range,
+            # source tokens strictly increasing within an expert
+            got = np.sort(slot[slot >= 0])
+            assert np.array_equal(got, np.arange(N))
+            for e in range(E):
+                seg = src[off[e]:off[e + 1]]
+                assert np.all(np.diff(seg) > 0)
+                es = slot[(idx == e) & (valid == 1)]
+                assert np.all((es >= off[e]) & (es < off[e + 1]))
+
+
+def test_layout_rejects_bad_dims():
+    idx = np.zeros((4, 2), np.int64)
+    with pytest.raises(ValueError):
+        oracle.layout(idx, 6, 4)
+
+
+def test_empty_input():
+    idx = np.zeros((0, 4), np.int64)
+    lay = oracle.layout(idx, 8, 2)
+    assert lay["num_tokens_per_expert"].sum() == 0 and lay["num_tokens_per_partition"].sum() == 0
+    off = oracle.expert_offsets(lay["num_tokens_per_expert"])
+    slot, src, ovf = oracle.slots(idx, lay["valid"], off, 0)
+    assert slot.size == 0 and ovf == 0
+
+
+# ----------------------------------------------------------------------------
+# dispatch / combine
+# ----------------------------------------------------------------------------
+
+def _pipeline(idx, w, x, E, P, use_fp8, cap=None):
+    return oracle.run_all(idx, w, x, E, P, use_fp8, capacity=cap)
+
+
+@pytest.mark.parametrize("use_fp8", [False, True])
+def test_dispatch_rows_are_the_source_rows(use_fp8):
+    T, H, E, K, P = 97, 384, 32, 4, 4
+    idx, w = workloads.random_case(7, T, E, K, mask_frac=0.1)
+    x = workloads.random_rows(8, T, H, "wide")
+    r = _pipeline(idx, w, x, E, P, use_fp8)
+    recv = r["recv_x"]
+    src = r["src_token"]
+    if not use_fp8:
+        assert np.array_equal(recv, x[src])
+    else:
+        for row in range(r["rows"]):
+            t = src[row]
+            for b in range(H // 128):
+                q, s = oracle.quant_block(x[t, b * 128:(b + 1) * 128])
+                assert np.array_equal(recv[row, b * 128:(b + 1) * 128], q)
+                assert r["recv_scales"][row, b] == s
+
+
+def test_dispatch_capacity_drops_rows():
+    T, H, E, K, P = 40, 128, 8, 3, 2
+    idx, w = workloads.random_case(17, T, E, K)
+    x = workloads.random_rows(18, T, H, "normal")
+    full = _pipeline(idx, w, x, E, P, False)
+    part = _pipeline(idx, w, x, E, P, False, cap=50)
+    assert part["overflow"] == 1 and part["rows"] == 50
+    assert np.array_equal(part["recv_x"], full["recv_x"][:50])
+
+
+@pytest.mark.parametrize("name", ["tiny", "skewed"])
+def test_bf16_round_trip_is_exact_identity(name):
+    """Identity experts and weights summing to 1: combine(dispatch(x)) == x
+    bit for bit (fp32 error ~K*2^-24 is far below half a BF16 ulp)."""
+    wl = workloads.config(name)
+    idx, w, x = workloads.make(wl)
+    r = _pipeline(idx, w, x, wl.E, wl.P, False)
+    out = oracle.combine(r["recv_x"], r["slot"], w)
+    live = (r["slot"] >= 0).any(axis=1)
+    wsum = w.astype(np.float64).sum(axis=1)
+    assert np.all(np.abs(wsum[live] - 1) <= wl.K * 2.0 ** -24)
+    assert np.array_equal(out[live], x[live])
+    assert np.all(out[~live] == 0)
+
+
+def test_fp8_round_trip_within_fp8_error():
+    wl = workloads.config("decode")
+    idx, w, x = workloads.make(wl)
+    r = _pipeline(idx, w, x, wl.E, wl.P, True)
+    nb = wl.H // 128
+    dq = np.empty((r["rows"], wl.H), np.float32)
+    lut = np.array([oracle.e4m3fn_decode(c) if (c & 0x7F) != 0x7F else 0.0 for c in range(256)], np.float32)
+    for b in range(nb):
+        dq[:, b * 128:(b + 1) * 128] = lut[r["recv_x"][:, b * 128:(b + 1) * 128]] * r["recv_scales"][:, b:b + 1]
+    y = workloads.bf16_bits_from_f32(dq)
+    out = _f32(oracle.combine(y, r["slot"], w)).astype(np.float64)
+    xf = _f32(x).astype(np.float64)
+    s_tok = np.repeat(r["recv_scales"][np.maximum(r["slot"][:, 0], 0)], 128, axis=1)
+    bound = 2.0 ** -4 * np.abs(xf) + 2.0 ** -10 * s_tok + 2.0 ** -7 * np.abs(xf) + 1e-30
+    assert np.all(np.abs(out - xf) <= bound)
+
+
+def test_adjoint_exact_on_small_integers():
+    """<dispatch(x), y> == <x, combine_{w=1}(y)> exactly when all values are
+    small integers (every product and sum is exact in fp32, bf16 and fp64)."""
+    rng = np.random.default_rng(4)
+    for T, E, K, P, H in [(33, 8, 3, 2, 16), (130, 64, 6, 8, 24), (64, 16, 16, 4, 8)]:
+        idx, _ = workloads.random_case(T, T, E, K, mask_frac=0.15, distinct=K <= E)
+        w = np.ones((T, K), np.float32)
+        x = workloads.bf16_bits_from_f32(rng.integers(-3, 4, (T, H)).astype(np.float32))
+        r = _pipeline(idx, w, x, E, P, False)
+        y = workloads.bf16_bits_from_f32(rng.integers(-3, 4, (r["rows"], H)).astype(np.float32))
+        lhs = (_f32(r["recv_x"]).astype(np.float64) * _f32(y)).sum()
+        cy = oracle.combine(y, r["slot"], w)
+        rhs = (_f32(x).astype(np.float64) * _f32(cy)).sum()
+        assert lhs == rhs
+
+
+def test_combine_is_gather_for_k1():
+    T, H, E = 50, 64, 10
+    idx, _ = workloads.random_case(3, T, E, 1, mask_frac=0.2)
+    w = np.ones((T, 1), np.float32)
+    r = _pipeline(idx, w, None, E, 2, False)
+    y = workloads.random_rows(5, r["rows"], H, "bits")
+    out = oracle.combine(y, r["slot"], w)
+    s = r["slot"][:, 0]
+    ref = torch.from_numpy(y.view(np.int16)).index_select(0, torch.from_numpy(np.maximum(s, 0).astype(np.int64))).numpy().view(np.uint16)
+    assert np.array_equal(out[s >= 0], ref[s >= 0])
+    # masked token -> +0 row (fma(w, y, +0) never runs)
+    assert np.all(out[s < 0] == 0)
+
+
+def test_combine_within_one_ulp_of_exact_sum():
+    T, H, E, K = 80, 256, 32, 8
+    idx, w = workloads.random_case(12, T, E, K, mask_frac=0.1)
+    r = _pipeline(idx, w, None, E, 4, False)
+    y = workloads.random_rows(13, r["rows"], H, "wide")
+    out = _f32(oracle.combine(y, r["slot"], w)).astype(np.float64)
+    yf = _f32(y).astype(np.float64)
+    exact = np.zeros((T, H))
+    for t in range(T):
+        for k in range(K):
+            s = r["slot"][t, k]
+            if s >= 0:
+                exact[t] += float(w[t, k]) * yf[s]
+    # 1 bf16 ulp of the exact value (8 significant bits), plus the fp32
+    # accumulation error bound K * 2^-24 * sum|w y|
+    mag = np.zeros((T, H))
+    for t in range(T):
+        for k in range(K):
+            s = r["slot"][t, k]
+            if s >= 0:
+                mag[t] += abs(float(w[t, k])) * np.abs(yf[s])
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 1e-38))) - 7)
+    assert np.all(np.abs(out - exact) <= ulp + K * 2.0 ** -24 * mag + 1e-38)
+
+
+def test_combine_pow2_weights_exact():
+    T, H, E, K = 40, 32, 16, 4
+    idx, w = workloads.random_case(14, T, E, K, weights="pow2")
+    r = _pipeline(idx, w, None, E, 4, False)
+    rng = np.random.default_rng(15)
+    y = workloads.bf16_bits_from_f32(rng.integers(-8, 9, (r["rows"], H)).astype(np.float32))
+    out = _f32(oracle.combine(y, r["slot"], w)).astype(np.float64)
+    yf = _f32(y).astype(np.float64)
+    exact = np.zeros((T, H))
+    for t in range(T):
+        for k in range(K):
+            exact[t] += float(w[t, k]) * yf[r["slot"][t, k]]
+    # every partial sum is a short dyadic number, so the fp32 fma chain is
+    # exact and the only rounding is the final one to bf16 (torch's RNE)
+    assert np.all(np.abs(exact) < 2 ** 10)
+    ref = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(out, ref.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------
+# the five workloads: invariants at full size
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "v3", "skewed", "large"])
+def test_workload_invariants(name):
+    wl = workloads.config(name)
+    idx, w, _ = workloads.make(wl, with_x=False)
+    lay = oracle.layout(idx, wl.E, wl.P)
+    masked = int((idx < 0).sum())
+    assert lay["num_invalid"] == 0
+    assert lay["num_tokens_per_expert"].sum() == wl.T * wl.K - masked
+    assert masked == int(np.floor(wl.mask_frac * wl.T * wl.K))
+    assert np.array_equal(lay["num_tokens_per_expert"], np.bincount(idx[idx >= 0], minlength=wl.E))
+    if name == "v3":
+        # group-limited gating: at most 4 of the 8 groups (= partitions)
+        assert lay["is_token_in_partition"].sum(axis=1).max() <= 4
+    if name == "skewed":
+        c = lay["num_tokens_per_expert"]
+        assert c.max() > 20 * max(c.min(), 1)
