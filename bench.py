@@ -1,0 +1,238 @@
+"""Benchmark: MoE dispatch + combine on one MI355X.
+
+One step runs the whole path once on resident synthetic inputs:
+    ep_get_dispatch_layout -> ep_dispatch (FP8) -> ep_combine -> ep_handle_recv_counts
+(the last one reads the per-expert counts back to the host and synchronises).
+`value` is logical GB/s over the step: the pages count every delivered payload
+byte, local traffic included (GeekNews, "Kết quả đo hiệu năng"), so
+    dispatch bytes = N * (H * b + 4 * H / 128 [FP8 scales]),  b = 1 (FP8) or 2 (BF16)
+    combine bytes  = N * H * 2
+with N the number of dispatched (token, k) pairs.
+
+Prints one JSON line.  Default workload: the V3 shape (8192 tokens, hidden
+7168, 256 experts, top-8, FP8 dispatch, BF16 combine).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch & combine logical GB/s on 1 MI355X (8192×7168 top-8); % HBM peak"
+HBM_PEAK_GBPS = 8000.0
+
+DESCR = {
+    "tiny": "tiny: T=128 H=256 E=16 top-2 P=4, softmax routing, BF16 dispatch",
+    "decode": "decode: T=128 H=7168 E=256 top-8 P=8, softmax routing, FP8 dispatch, BF16 combine",
+    "v3": "v3: T=8192 H=7168 E=256 top-8 P=8, group-limited gating (4 of 8 groups), FP8 dispatch, BF16 combine",
+    "skewed": "skewed: T=4096 H=4096 E=64 top-6 P=8, Zipf(1.2) popularity, 5% masked, BF16 dispatch/combine",
+    "large": "large: T=16384 H=7168 E=256 top-8 P=16, uniform routing, Dirichlet(1) weights, FP8 dispatch, BF16 combine",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="v3", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def byte_counts(wl, N):
+    T, H, K, E, P = wl.T, wl.H, wl.K, wl.E, wl.P
+    b = 1 if wl.use_fp8 else 2
+    nb = H // 128
+    B = (T + 255) // 256
+    disp_logical = N * (H * b + (4 * nb if wl.use_fp8 else 0))
+    comb_logical = N * H * 2
+    # algorithmic HBM bytes of each call (each byte the definition must read or write once)
+    layout_alg = T * K * 8 + T * P + T * K * 4 + B * (E + P + 1) * 4 * 2 + (2 * E + P + 8) * 4
+    dispatch_alg = (T * H * 2 + disp_logical + T * K * 4 + T * K * 4 * 2 + T * K * 4 + N * 4
+                    + (E + 1) * 4 + B * E * 4)
+    combine_alg = N * H * 2 + T * H * 2 + T * K * 8
+    return dict(dispatch_logical=disp_logical, combine_logical=comb_logical,
+                layout_alg=layout_alg, dispatch_alg=dispatch_alg, combine_alg=combine_alg)
+
+
+def cpu_baseline(wl, idx, w, x, y, runs):
+    """The oracle, single-threaded, on the full workload: one whole step per run."""
+    import oracle
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        r = oracle.run_all(idx, w, x, wl.E, wl.P, wl.use_fp8)
+        oracle.combine(y, r["slot"], w)
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times), r["N"]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the path runs on one MI355X and is not sharded across GPUs.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_get_dispatch_scan_amd as ep
+    import workloads
+
+    ep.load()
+    dev = torch.device("cuda:0")
+    wl = workloads.config(args.config)
+    print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    y = workloads.expert_outputs(wl, N)
+    T, H, K, E, P = wl.T, wl.H, wl.K, wl.E, wl.P
+    cap = T * K
+
+    t_idx = torch.from_numpy(idx).to(dev)
+    t_w = torch.from_numpy(w).to(dev)
+    t_x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    t_y = torch.from_numpy(y.view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = torch.empty(ep.ep_workspace_bytes(T, K, E, P), dtype=torch.uint8, device=dev)
+    ntpp = torch.empty(P, dtype=torch.int32, device=dev)
+    ntpe = torch.empty(E, dtype=torch.int32, device=dev)
+    itip = torch.empty((T, P), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    if wl.use_fp8:
+        recv = torch.empty((cap, H), dtype=torch.uint8, device=dev)
+        scales = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
+    else:
+        recv = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        scales = None
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    counts = (ctypes.c_int32 * E)()
+    nrecv = ctypes.c_int32(0)
+    h = ep.ep_handle_t()
+    stream = torch.cuda.current_stream()
+    sp = ep._stream()
+    p = lambda t: None if t is None else t.data_ptr()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = ep.ep_get_dispatch_layout(p(t_idx), T, K, E, P, p(ntpp), p(ntpe), p(itip), p(ninv),
+                                       p(ws), ws.numel(), h, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= ep.ep_dispatch(p(t_x), p(t_w), H, int(wl.use_fp8), p(recv), p(scales), cap, h, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        rc |= ep.ep_combine(p(t_y), h, None, p(out), sp)
+        if ev is not None:
+            ev[3].record(stream)
+        rc |= ep.ep_handle_recv_counts(h, counts, ctypes.byref(nrecv), sp)
+        if rc != 0:
+            raise RuntimeError(f"step failed: {ep.ep_last_error()}")
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert nrecv.value == N, (nrecv.value, N)
+
+    # timed region: exactly K steps, wall clock, synchronised on both sides
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    lay_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    disp_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    bc = byte_counts(wl, N)
+    mean = lambda v: sum(v) / len(v)
+    phases = {"layout": mean(lay_ms), "dispatch": mean(disp_ms), "combine": mean(comb_ms)}
+    # dominant kernel: the call with the largest share of the step (each of
+    # dispatch and combine is a single kernel launch)
+    dom = max(("dispatch", "combine"), key=lambda k: phases[k])
+    dom_bytes = bc["dispatch_alg"] if dom == "dispatch" else bc["combine_alg"]
+    dom_gbps = dom_bytes / (phases[dom] * 1e-3) / 1e9
+    dom_kernel = {"dispatch": "dispatch_fp8_kernel" if wl.use_fp8 else "dispatch_bf16_kernel",
+                  "combine": "combine_kernel"}[dom]
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    logical = bc["dispatch_logical"] + bc["combine_logical"]
+    value = logical / (ms_per_step * 1e-3) / 1e9
+    alg_step = bc["layout_alg"] + bc["dispatch_alg"] + bc["combine_alg"]
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16/fp32-acc" if wl.use_fp8 else "bf16/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": DESCR[args.config], "tokens": T, "hidden": H, "experts": E,
+                   "topk": K, "partitions": P, "dispatched_pairs": N,
+                   "fp8_dispatch": bool(wl.use_fp8), "capacity_rows": cap},
+        "roofline": {
+            "bound": "hbm", "kernel": dom_kernel,
+            "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "bytes_per_launch": dom_bytes, "avg_launch_us": round(phases[dom] * 1e3, 2),
+            "traffic": None,
+        },
+        "phases_us": {k: round(v * 1e3, 2) for k, v in phases.items()},
+        "logical_GBps": {
+            "dispatch": round(bc["dispatch_logical"] / ((phases["layout"] + phases["dispatch"]) * 1e-3) / 1e9, 1),
+            "combine": round(bc["combine_logical"] / (phases["combine"] * 1e-3) / 1e9, 1),
+        },
+        "hbm_frac_step": round(alg_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "hbm_frac_kernels": {
+            "dispatch": round(bc["dispatch_alg"] / (phases["dispatch"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "combine": round(bc["combine_alg"] / (phases["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline ({args.cpu_runs} oracle runs)", file=sys.stderr, flush=True)
+        sec, n_cpu = cpu_baseline(wl, idx, w, x, y, args.cpu_runs)
+        assert n_cpu == N
+        res["cpu_baseline"] = {
+            "value": round(logical / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole step (layout, slots, {'FP8' if wl.use_fp8 else 'BF16'} dispatch, combine) "
+                      f"on the full {args.config} workload, single thread, median of {args.cpu_runs} runs "
+                      f"({sec:.2f} s each); host {platform.processor() or platform.machine()}, "
+                      f"{os.cpu_count()} logical CPUs visible",
+        }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,311 @@
+"""Python binding of libmoe_ep: MoE dispatch / combine on one MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+``libmoe_ep.so`` (built from ``csrc/`` for gfx950); PyTorch supplies device
+memory and the stream.  There is no CPU fallback: if the library is missing
+the calls raise.
+
+Two layers:
+
+* ``ep_*`` -- one function per C entry point of ``include/moe_ep.h``, same
+  names and arguments (device pointers as ints, the stream as a handle).
+* ``get_dispatch_layout`` / ``dispatch`` / ``dispatch_cached`` / ``combine`` /
+  ``handle_recv_counts`` -- the same calls on torch tensors: they allocate
+  the outputs with ``torch.empty`` on the tensors' device and launch on torch's
+  current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+from . import _build
+
+LIB_PATH = _build.LIB_PATH
+
+EP_OK = 0
+EP_EINVAL = -1
+EP_EHIP = -2
+EP_ECAPACITY = -3
+EP_EIDS = -4
+EP_HANDLE_MAGIC = 0x31485045
+
+
+class EpError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe_ep error {code}: {msg}")
+        self.code = code
+
+
+class ep_handle_t(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("stage", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_partitions", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("use_fp8", ctypes.c_int32),
+        ("capacity_rows", ctypes.c_int32),
+        ("has_weights", ctypes.c_int32),
+        ("num_chunks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
+        ("expert_offset", ctypes.c_void_p),
+        ("slot", ctypes.c_void_p),
+        ("src_token", ctypes.c_void_p),
+        ("weights", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+        ("pair_code", ctypes.c_void_p),
+        ("chunk_base", ctypes.c_void_p),
+        ("chunk_pcnt", ctypes.c_void_p),
+        ("chunk_inv", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+# C entry points and their ctypes signatures
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGS = {
+    "ep_version": ([], _I),
+    "ep_last_error": ([], ctypes.c_char_p),
+    "ep_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
+    "ep_get_dispatch_layout": ([_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                ctypes.POINTER(ep_handle_t), _P], _I),
+    "ep_dispatch": ([_P, _P, _I, _I, _P, _P, _I, ctypes.POINTER(ep_handle_t), _P], _I),
+    "ep_dispatch_cached": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_combine": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_handle_recv_counts": ([ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_e4m3fn_encode": ([_P, _P, ctypes.c_int64, _P], _I),
+}
+
+
+def load():
+    """Load libmoe_ep.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, ok=(EP_OK,)):
+    if rc not in ok:
+        raise EpError(rc, load().ep_last_error().decode())
+    return rc
+
+
+# ----------------------------------------------------------------------------
+# the C entry points
+# ----------------------------------------------------------------------------
+
+def ep_version() -> int:
+    return load().ep_version()
+
+
+def ep_last_error() -> str:
+    return load().ep_last_error().decode()
+
+
+def ep_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int, num_partitions: int) -> int:
+    return load().ep_workspace_bytes(num_tokens, num_topk, num_experts, num_partitions)
+
+
+def ep_get_dispatch_layout(topk_idx, num_tokens, num_topk, num_experts, num_partitions,
+                           num_tokens_per_partition, num_tokens_per_expert,
+                           is_token_in_partition, num_invalid, ws, ws_bytes, handle, stream) -> int:
+    return load().ep_get_dispatch_layout(topk_idx, num_tokens, num_topk, num_experts,
+                                         num_partitions, num_tokens_per_partition,
+                                         num_tokens_per_expert, is_token_in_partition,
+                                         num_invalid, ws, ws_bytes, ctypes.byref(handle), stream)
+
+
+def ep_dispatch(x, topk_weights, hidden, use_fp8, recv_x, recv_scales, capacity_rows, handle,
+                stream) -> int:
+    return load().ep_dispatch(x, topk_weights, hidden, int(use_fp8), recv_x, recv_scales,
+                              capacity_rows, ctypes.byref(handle), stream)
+
+
+def ep_dispatch_cached(x, handle, recv_x, recv_scales, stream) -> int:
+    return load().ep_dispatch_cached(x, ctypes.byref(handle), recv_x, recv_scales, stream)
+
+
+def ep_combine(y, handle, topk_weights, out, stream) -> int:
+    return load().ep_combine(y, ctypes.byref(handle), topk_weights, out, stream)
+
+
+def ep_handle_recv_counts(handle, host_counts, host_num_recv, stream) -> int:
+    return load().ep_handle_recv_counts(ctypes.byref(handle), host_counts, host_num_recv, stream)
+
+
+def ep_e4m3fn_encode(inp, out, n, stream) -> int:
+    return load().ep_e4m3fn_encode(inp, out, n, stream)
+
+
+# ----------------------------------------------------------------------------
+# the same calls on torch tensors
+# ----------------------------------------------------------------------------
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class Handle:
+    """Routing metadata of one dispatch (wraps ep_handle_t and keeps the
+    workspace it points into alive)."""
+    c: ep_handle_t
+    ws: object
+
+    @property
+    def num_tokens(self):
+        return self.c.num_tokens
+
+    @property
+    def num_topk(self):
+        return self.c.num_topk
+
+    @property
+    def hidden(self):
+        return self.c.hidden
+
+    def _view(self, field, n, dtype):
+        import torch
+        if n == 0:
+            return torch.empty(0, dtype=dtype, device=self.ws.device)
+        off = getattr(self.c, field) - self.ws.data_ptr()
+        return self.ws[off:off + n * 4].view(dtype)
+
+    @property
+    def slot(self):
+        import torch
+        return self._view("slot", self.num_tokens * self.num_topk, torch.int32).view(self.num_tokens, self.num_topk)
+
+    @property
+    def src_token(self):
+        import torch
+        return self._view("src_token", self.num_tokens * self.num_topk, torch.int32)
+
+    @property
+    def expert_offset(self):
+        import torch
+        return self._view("expert_offset", self.c.num_experts + 1, torch.int32)
+
+    @property
+    def weights(self):
+        import torch
+        return self._view("weights", self.num_tokens * self.num_topk, torch.float32).view(self.num_tokens, self.num_topk)
+
+
+@dataclass
+class Layout:
+    num_tokens_per_partition: object
+    num_tokens_per_expert: object
+    is_token_in_partition: object
+    num_invalid: object
+    handle: Handle
+
+
+def get_dispatch_layout(topk_idx, num_experts: int, num_partitions: int, ws=None) -> Layout:
+    """topk_idx: int64 [T, K] on the GPU.  Returns the counts, the mask and a
+    handle for ``dispatch``.  ``ws`` (uint8, >= ep_workspace_bytes) may be
+    passed to reuse a workspace."""
+    import torch
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    nbytes = ep_workspace_bytes(T, K, num_experts, num_partitions)
+    if nbytes == 0:
+        raise EpError(EP_EINVAL, f"invalid dims T={T} K={K} E={num_experts} P={num_partitions}")
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ntpp = torch.empty(num_partitions, dtype=torch.int32, device=dev)
+    ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    itip = torch.empty((T, num_partitions), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    h = ep_handle_t()
+    _check(ep_get_dispatch_layout(_ptr(topk_idx.contiguous()), T, K, num_experts, num_partitions,
+                                  _ptr(ntpp), _ptr(ntpe), _ptr(itip), _ptr(ninv), _ptr(ws),
+                                  ws.numel(), h, _stream()))
+    return Layout(ntpp, ntpe, itip, ninv, Handle(h, ws))
+
+
+def dispatch(x, topk_weights, layout: Layout, use_fp8: bool, capacity_rows: Optional[int] = None):
+    """x: bf16 [T, H]; topk_weights: fp32 [T, K] or None.
+    Returns (recv_x, recv_scales or None, handle).  recv_x is float8_e4m3fn
+    [capacity, H] in FP8 mode, else bf16 [capacity, H]; capacity defaults to
+    T*K (no host sync)."""
+    import torch
+    h = layout.handle
+    T, H = x.shape
+    K = h.num_topk
+    cap = T * K if capacity_rows is None else int(capacity_rows)
+    dev = x.device
+    if use_fp8:
+        recv = torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev)
+        scales = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
+    else:
+        recv = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        scales = None
+    _check(ep_dispatch(_ptr(x), _ptr(topk_weights), H, int(use_fp8), _ptr(recv), _ptr(scales),
+                       cap, h.c, _stream()))
+    return recv, scales, h
+
+
+def dispatch_cached(x, handle: Handle, recv_x=None, recv_scales=None):
+    """Re-send new rows along a dispatched handle's routing."""
+    import torch
+    c = handle.c
+    cap, H = c.capacity_rows, c.hidden
+    if recv_x is None:
+        recv_x = torch.empty((cap, H), dtype=torch.float8_e4m3fn if c.use_fp8 else torch.bfloat16,
+                             device=x.device)
+    if c.use_fp8 and recv_scales is None:
+        recv_scales = torch.empty((cap, H // 128), dtype=torch.float32, device=x.device)
+    _check(ep_dispatch_cached(_ptr(x), c, _ptr(recv_x), _ptr(recv_scales), _stream()))
+    return recv_x, recv_scales
+
+
+def combine(y, handle: Handle, topk_weights=None, out=None):
+    """y: bf16 [rows, H] in dispatch's receive order.  Returns bf16 [T, H]."""
+    import torch
+    c = handle.c
+    if out is None:
+        out = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=y.device)
+    _check(ep_combine(_ptr(y), c, _ptr(topk_weights), _ptr(out), _stream()))
+    return out
+
+
+def handle_recv_counts(handle: Handle):
+    """Synchronises the current stream.  Returns (counts list[E], N, status)
+    where status is EP_OK, EP_ECAPACITY or EP_EIDS."""
+    E = handle.c.num_experts
+    counts = (ctypes.c_int32 * E)()
+    n = ctypes.c_int32(0)
+    rc = _check(ep_handle_recv_counts(handle.c, counts, ctypes.byref(n), _stream()),
+                ok=(EP_OK, EP_ECAPACITY, EP_EIDS))
+    return list(counts), int(n.value), rc
+
+
+def e4m3fn_encode(v):
+    """fp32 tensor -> uint8 codes with the device encoder."""
+    import torch
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(ep_e4m3fn_encode(_ptr(v.contiguous()), _ptr(out), v.numel(), _stream()))
+    return out

@@ -1,0 +1,323 @@
+// The moe_ep C ABI: argument validation, workspace carving, handle upkeep and
+// kernel launches.  Nothing here allocates device memory or synchronises,
+// except ep_handle_recv_counts (a small device-to-host copy).
+#include "moe_ep.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(EP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kChunk = 256;
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+    size_t chunk_cnt, chunk_pcnt, chunk_inv, pair_code, expert_offset, slot, src_token,
+        weights, status, total;
+};
+
+bool dims_ok(int T, int K, int E, int P)
+{
+    return T >= 0 && K >= 1 && K <= EP_MAX_TOPK && E >= 1 && E <= EP_MAX_EXPERTS && P >= 1 &&
+           P <= EP_MAX_PARTITIONS && E % P == 0 && (int64_t)T * K < (int64_t)1 << 31;
+}
+
+int check_dims(int T, int K, int E, int P)
+{
+    if (dims_ok(T, K, E, P))
+        return EP_OK;
+    return fail(EP_EINVAL,
+                "invalid dims T=%d K=%d E=%d P=%d (need T>=0, 1<=K<=%d, 1<=E<=%d, "
+                "1<=P<=%d, E%%P==0, T*K<2^31)",
+                T, K, E, P, EP_MAX_TOPK, EP_MAX_EXPERTS, EP_MAX_PARTITIONS);
+}
+
+WsLayout ws_layout(int T, int K, int E, int P)
+{
+    const size_t B = (size_t)(T + kChunk - 1) / kChunk;
+    const size_t TK = (size_t)T * K;
+    WsLayout L;
+    size_t o = 0;
+    L.chunk_cnt = o;     o += up(B * E * 4);
+    L.chunk_pcnt = o;    o += up(B * P * 4);
+    L.chunk_inv = o;     o += up(B * 4);
+    L.pair_code = o;     o += up(TK * 4);
+    L.expert_offset = o; o += up(((size_t)E + 1) * 4);
+    L.slot = o;          o += up(TK * 4);
+    L.src_token = o;     o += up(TK * 4);
+    L.weights = o;       o += up(TK * 4);
+    L.status = o;        o += up(4 * 4);
+    L.total = o;
+    return L;
+}
+
+int check_handle(const ep_handle_t* h, int min_stage)
+{
+    if (!h)
+        return fail(EP_EINVAL, "handle is NULL");
+    if (h->magic != EP_HANDLE_MAGIC)
+        return fail(EP_EINVAL, "handle was not filled by ep_get_dispatch_layout");
+    if (h->stage < min_stage)
+        return fail(EP_EINVAL, "handle has not been dispatched yet (call ep_dispatch first)");
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_version(void) { return 10000; }
+
+const char* ep_last_error(void) { return g_err.c_str(); }
+
+size_t ep_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_partitions)
+{
+    if (!dims_ok(num_tokens, num_topk, num_experts, num_partitions))
+        return 0;
+    return ws_layout(num_tokens, num_topk, num_experts, num_partitions).total;
+}
+
+int ep_get_dispatch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
+                           int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
+                           uint8_t* is_token_in_partition, int32_t* num_invalid,
+                           void* ws, size_t ws_bytes, ep_handle_t* handle,
+                           hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_dims(T, K, E, P);
+    if (rc)
+        return rc;
+    if (!handle)
+        return fail(EP_EINVAL, "handle is NULL");
+    if (T > 0 && (!topk_idx || !aligned(topk_idx, 8)))
+        return fail(EP_EINVAL, "topk_idx must be a non-NULL 8-byte aligned device pointer");
+    if (T > 0 && !is_token_in_partition)
+        return fail(EP_EINVAL, "is_token_in_partition is NULL");
+    if (!num_tokens_per_partition || !num_tokens_per_expert || !num_invalid ||
+        !aligned(num_tokens_per_partition, 4) || !aligned(num_tokens_per_expert, 4) ||
+        !aligned(num_invalid, 4))
+        return fail(EP_EINVAL, "count outputs must be non-NULL 4-byte aligned device pointers");
+    const WsLayout L = ws_layout(T, K, E, P);
+    if (!ws || !aligned(ws, kAlign))
+        return fail(EP_EINVAL, "workspace must be a non-NULL 256-byte aligned device pointer");
+    if (ws_bytes < L.total)
+        return fail(EP_EINVAL, "workspace too small: %zu bytes given, %zu needed", ws_bytes, L.total);
+
+    char* w = static_cast<char*>(ws);
+    ep_handle_t h;
+    memset(&h, 0, sizeof h);
+    h.magic = EP_HANDLE_MAGIC;
+    h.stage = 1;
+    h.num_tokens = T;
+    h.num_topk = K;
+    h.num_experts = E;
+    h.num_partitions = P;
+    h.num_chunks = (T + kChunk - 1) / kChunk;
+    h.ws = ws;
+    h.ws_bytes = ws_bytes;
+    h.expert_offset = reinterpret_cast<int32_t*>(w + L.expert_offset);
+    h.slot = reinterpret_cast<int32_t*>(w + L.slot);
+    h.src_token = reinterpret_cast<int32_t*>(w + L.src_token);
+    h.weights = reinterpret_cast<float*>(w + L.weights);
+    h.status = reinterpret_cast<int32_t*>(w + L.status);
+    h.pair_code = reinterpret_cast<int32_t*>(w + L.pair_code);
+    h.chunk_base = reinterpret_cast<int32_t*>(w + L.chunk_cnt);
+    h.chunk_pcnt = reinterpret_cast<int32_t*>(w + L.chunk_pcnt);
+    h.chunk_inv = reinterpret_cast<int32_t*>(w + L.chunk_inv);
+
+    hipError_t e = moe_ep::launch_layout(topk_idx, T, K, E, P, is_token_in_partition,
+                                         h.pair_code, h.chunk_base, h.chunk_pcnt, h.chunk_inv,
+                                         h.expert_offset, num_tokens_per_expert,
+                                         num_tokens_per_partition, num_invalid, h.status, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "layout launch");
+    *handle = h;
+    return EP_OK;
+}
+
+static int check_rows(const ep_handle_t* h, const void* x, int H, int use_fp8, const void* recv_x,
+                      const float* recv_scales, int capacity)
+{
+    const int T = h->num_tokens;
+    if (H < 1 || H > EP_MAX_HIDDEN || H % 8 != 0)
+        return fail(EP_EINVAL, "hidden=%d must be in [1, %d] and a multiple of 8", H, EP_MAX_HIDDEN);
+    if (use_fp8 != 0 && use_fp8 != 1)
+        return fail(EP_EINVAL, "use_fp8 must be 0 or 1");
+    if (use_fp8 && H % 128 != 0)
+        return fail(EP_EINVAL, "FP8 dispatch needs hidden %% 128 == 0 (hidden=%d)", H);
+    if (capacity < 0 || (int64_t)capacity > (int64_t)T * h->num_topk)
+        return fail(EP_EINVAL, "capacity_rows=%d must be in [0, T*K=%lld]", capacity,
+                    (long long)T * h->num_topk);
+    if (T > 0 && (!x || !aligned(x, 16)))
+        return fail(EP_EINVAL, "x must be a non-NULL 16-byte aligned device pointer");
+    if (capacity > 0 && (!recv_x || !aligned(recv_x, 16)))
+        return fail(EP_EINVAL, "recv_x must be a non-NULL 16-byte aligned device pointer");
+    if (use_fp8 && capacity > 0 && (!recv_scales || !aligned(recv_scales, 4)))
+        return fail(EP_EINVAL, "recv_scales must be a non-NULL 4-byte aligned device pointer");
+    return EP_OK;
+}
+
+static int run_dispatch(const ep_handle_t* h, const void* x, const float* w_in, void* recv_x,
+                        float* recv_scales, bool fresh, hipStream_t stream)
+{
+    moe_ep::DispatchLaunch L;
+    L.x = x;
+    L.T = h->num_tokens;
+    L.H = h->hidden;
+    L.K = h->num_topk;
+    L.E = h->num_experts;
+    L.use_fp8 = h->use_fp8;
+    L.fresh = fresh;
+    L.capacity = h->capacity_rows;
+    L.pair_code = h->pair_code;
+    L.chunk_base = h->chunk_base;
+    L.expert_offset = h->expert_offset;
+    L.w_in = w_in;
+    L.w_copy = h->weights;
+    L.slot = h->slot;
+    L.src_token = h->src_token;
+    L.status = h->status;
+    L.recv = recv_x;
+    L.scales = recv_scales;
+    hipError_t e = moe_ep::launch_dispatch(L, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "dispatch launch");
+    return EP_OK;
+}
+
+int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp8,
+                void* recv_x, float* recv_scales, int capacity_rows,
+                ep_handle_t* handle, hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 1);
+    if (rc)
+        return rc;
+    rc = check_rows(handle, x, hidden, use_fp8, recv_x, recv_scales, capacity_rows);
+    if (rc)
+        return rc;
+    if (topk_weights && !aligned(topk_weights, 4))
+        return fail(EP_EINVAL, "topk_weights must be 4-byte aligned");
+    ep_handle_t h = *handle;
+    h.hidden = hidden;
+    h.use_fp8 = use_fp8;
+    h.capacity_rows = capacity_rows;
+    h.has_weights = topk_weights != nullptr;
+    rc = run_dispatch(&h, x, topk_weights, recv_x, recv_scales, true, stream);
+    if (rc)
+        return rc;
+    h.stage = 2;
+    *handle = h;
+    return EP_OK;
+}
+
+int ep_dispatch_cached(const void* x, const ep_handle_t* handle, void* recv_x, float* recv_scales,
+                       hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 2);
+    if (rc)
+        return rc;
+    rc = check_rows(handle, x, handle->hidden, handle->use_fp8, recv_x, recv_scales,
+                    handle->capacity_rows);
+    if (rc)
+        return rc;
+    return run_dispatch(handle, x, nullptr, recv_x, recv_scales, false, stream);
+}
+
+int ep_combine(const void* y, const ep_handle_t* handle, const float* topk_weights, void* out,
+               hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 2);
+    if (rc)
+        return rc;
+    const int T = handle->num_tokens;
+    const float* w = topk_weights ? topk_weights : (handle->has_weights ? handle->weights : nullptr);
+    if (!w && T > 0)
+        return fail(EP_EINVAL, "no weights: pass topk_weights or give them to ep_dispatch");
+    if (w && !aligned(w, 4))
+        return fail(EP_EINVAL, "topk_weights must be 4-byte aligned");
+    if (T > 0 && (!out || !aligned(out, 16)))
+        return fail(EP_EINVAL, "out must be a non-NULL 16-byte aligned device pointer");
+    if (T > 0 && handle->capacity_rows > 0 && (!y || !aligned(y, 16)))
+        return fail(EP_EINVAL, "y must be a non-NULL 16-byte aligned device pointer");
+    hipError_t e = moe_ep::launch_combine(y, T, handle->hidden, handle->num_topk, handle->slot, w,
+                                          out, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "combine launch");
+    return EP_OK;
+}
+
+int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts, int32_t* host_num_recv,
+                          hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 1);
+    if (rc)
+        return rc;
+    const int E = handle->num_experts;
+    int32_t off[EP_MAX_EXPERTS + 1];
+    int32_t st[4];
+    hipError_t e = hipMemcpyAsync(off, handle->expert_offset, sizeof(int32_t) * (E + 1),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(st, handle->status, sizeof st, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "reading counts");
+    if (host_counts)
+        for (int i = 0; i < E; ++i)
+            host_counts[i] = off[i + 1] - off[i];
+    if (host_num_recv)
+        *host_num_recv = off[E];
+    if (handle->stage >= 2 && st[0])
+        return fail(EP_ECAPACITY, "dispatch dropped pairs: N=%d > capacity_rows=%d", off[E],
+                    handle->capacity_rows);
+    if (st[1] > 0)
+        return fail(EP_EIDS, "topk_idx held %d out-of-range or repeated ids", st[1]);
+    return EP_OK;
+}
+
+int ep_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream)
+{
+    g_err.clear();
+    if (n < 0)
+        return fail(EP_EINVAL, "n must be >= 0");
+    if (n > 0 && (!in || !out || !aligned(in, 4)))
+        return fail(EP_EINVAL, "in/out must be non-NULL device pointers (in 4-byte aligned)");
+    hipError_t e = moe_ep::launch_e4m3fn_encode(in, out, n, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "e4m3fn encode launch");
+    return EP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// combine on gfx950: gather each token's expert-output rows and reduce them.
+//
+// combine reduces the expert outputs back to the token's origin (GeekNews
+// usage section; stakiran github-trend-summarizer section 3: combine(y,
+// handle)), in BF16 with fp32 accumulation (aikraft.ru "Технические детали и
+// требования": BF16 combine).  Per token and channel:
+//     acc = +0.0f;  for k ascending with slot >= 0: acc = fma(w[t,k], y[slot][j], acc)
+//     out[t][j] = bf16_rne(acc)
+//
+// Work item = (token, segment of the row), one wave each.  Lanes 0..K-1 read
+// the token's receive rows and weights, which are broadcast to the wave as
+// scalars.  Each lane owns 8 channels per wave step; all K 16-byte gathers of
+// a step (and of kCombineUnroll steps) are issued before the first fma.
+#include "device.h"
+#include "launch.h"
+
+namespace moe_ep {
+
+constexpr int kCombineWaves = 4;
+constexpr int kCombineChPerIter = kWave * 8;     // 512 channels per wave step
+constexpr int kCombineUnroll = 2;
+
+struct CombineArgs {
+    const uint16_t* y;
+    int T, H, K;
+    int nseg, iters_per_seg, iters;
+    const int32_t* slot;
+    const float* w;
+    uint16_t* out;
+};
+
+template <int KMAX>
+__global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineArgs a)
+{
+    const int wi = blockIdx.x * kCombineWaves + threadIdx.x / kWave;
+    const int t = wi / a.nseg;
+    const int seg = wi % a.nseg;
+    if (t >= a.T)
+        return;
+    const int lane = lane_id();
+    int s_own = -1;
+    float w_own = 0.0f;
+    if (lane < a.K) {
+        s_own = a.slot[(size_t)t * a.K + lane];
+        w_own = a.w[(size_t)t * a.K + lane];
+    }
+    int sk[KMAX];
+    float wk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+        wk[k] = k < a.K ? readlane_f(w_own, k) : 0.0f;
+    }
+
+    const int H = a.H;
+    uint16_t* orow = a.out + (size_t)t * H;
+    const int i_begin = seg * a.iters_per_seg;
+    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
+
+    for (int i0 = i_begin; i0 < i_end; i0 += kCombineUnroll) {
+        u32x4 d[kCombineUnroll][KMAX];
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const int cb = (i0 + u) * kCombineChPerIter + lane * 8;
+            const bool active = (i0 + u < i_end) && cb < H;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (sk[k] >= 0 && active)
+                    d[u][k] = load16_nt(a.y + (size_t)sk[k] * H + cb);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const int cb = (i0 + u) * kCombineChPerIter + lane * 8;
+            const bool active = (i0 + u < i_end) && cb < H;
+            float acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (sk[k] >= 0 && active) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[2 * j] = __builtin_fmaf(wk[k], bf16_lo(d[u][k][j]), acc[2 * j]);
+                        acc[2 * j + 1] = __builtin_fmaf(wk[k], bf16_hi(d[u][k][j]), acc[2 * j + 1]);
+                    }
+                }
+            }
+            if (active) {
+                u32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+                store16_nt(orow + cb, o);
+            }
+        }
+    }
+}
+
+hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
+                          const float* w, void* out, hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    CombineArgs a;
+    a.y = static_cast<const uint16_t*>(y);
+    a.T = T;
+    a.H = H;
+    a.K = K;
+    a.slot = slot;
+    a.w = w;
+    a.out = static_cast<uint16_t*>(out);
+    a.iters = (H + kCombineChPerIter - 1) / kCombineChPerIter;
+    const int target_waves = 8192;
+    int want = (target_waves + T - 1) / T;
+    int n = want > a.iters ? a.iters : want;
+    if (n < 1)
+        n = 1;
+    a.iters_per_seg = (a.iters + n - 1) / n;
+    a.nseg = (a.iters + a.iters_per_seg - 1) / a.iters_per_seg;
+    const long long items = (long long)T * a.nseg;
+    dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
+    dim3 block(kCombineWaves * kWave);
+    if (K <= 2) hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a);
+    else if (K <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a);
+    else if (K <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe_ep

@@ -1,0 +1,87 @@
+// Device helpers shared by the moe_ep kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_ep {
+
+constexpr int kWave = 64;
+constexpr int kChunk = 256;        // tokens per layout workgroup (4 waves)
+constexpr int kChunkWaves = kChunk / kWave;
+constexpr int kQBlock = 128;       // channels per FP8 scale
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int readlane(int v, int lane)
+{
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// 16-byte streaming accesses.  The data of the permute and the gather is
+// touched once, so loads and stores are marked non-temporal.
+__device__ __forceinline__ u32x4 load16_nt(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void store16_nt(void* p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p)
+{
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// BF16 <-> fp32.  Widening is exact; narrowing rounds to nearest, ties to
+// even, on the 16 dropped bits (operands are finite by contract).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// fp32 -> OCP E4M3FN (bias 7, 3 mantissa bits, max 448, no infinities),
+// round to nearest even, saturating to +-448, sign of zero kept.
+//  |v| >= 448        -> 0x7E
+//  |v| in [2^-6,448) -> RNE on the 20 low mantissa bits of the fp32 pattern;
+//                       the fp32 exponent (bias 127) maps to bias 7 by
+//                       subtracting 120 << 3 from the top 12 bits
+//  |v| < 2^-6        -> subnormal code n = rint(|v| * 2^9) in 0..8 (8 is the
+//                       smallest normal, whose code is also 8)
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {                     // 448.0
+        code = 0x7Eu;
+    } else if (a >= 0x3C800000u) {              // 2^-6
+        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);
+    } else {
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    }
+    return sign | code;
+}
+
+}  // namespace moe_ep

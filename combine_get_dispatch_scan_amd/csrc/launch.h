@@ -1,0 +1,42 @@
+// Host-side launchers of the moe_ep kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_ep {
+
+// get_dispatch_layout: per-chunk count kernel + one-workgroup scan kernel.
+hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
+                         uint8_t* is_token_in_partition, int32_t* pair_code,
+                         int32_t* chunk_cnt, int32_t* chunk_pcnt, int32_t* chunk_inv,
+                         int32_t* expert_offset, int32_t* num_tokens_per_expert,
+                         int32_t* num_tokens_per_partition, int32_t* num_invalid,
+                         int32_t* status, hipStream_t stream);
+
+struct DispatchLaunch {
+    const void* x;
+    int T, H, K, E;
+    int use_fp8;
+    bool fresh;               // compute slots from pair codes (else reuse slot[])
+    int capacity;
+    const int32_t* pair_code;
+    const int32_t* chunk_base;
+    const int32_t* expert_offset;
+    const float* w_in;
+    float* w_copy;
+    int32_t* slot;
+    int32_t* src_token;
+    int32_t* status;
+    void* recv;
+    float* scales;
+};
+
+hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
+                          const float* w, void* out, hipStream_t stream);
+
+hipError_t launch_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace moe_ep

@@ -1,0 +1,275 @@
+// get_dispatch_layout on gfx950: per-chunk counting and the chunk-column scan.
+//
+// The layout step turns topk_idx into the per-destination counts that
+// dispatch consumes (stakiran github-trend-summarizer, "DeepEP 要約",
+// section 3: get_dispatch_layout precedes dispatch; GeekNews usage section:
+// per-expert counts feed the grouped GEMM).  The slot of each (token, k) pair
+// is the exclusive prefix of all earlier pairs of the same expert in token
+// order.  It is split as
+//     slot = expert_offset[e] + chunk_base[c][e] + rank_in_chunk
+// where c is the pair's 256-token chunk.  layout_chunk_kernel computes the
+// rank and the per-chunk counts with lane bitmaps in LDS (no global atomics,
+// so the result does not depend on scheduling); scan_kernel turns the counts
+// into chunk_base and expert_offset.
+#include "device.h"
+#include "launch.h"
+
+namespace moe_ep {
+
+// One workgroup of 256 threads per chunk of 256 tokens; thread i owns token
+// c*256 + i.  LDS holds, per expert, four 64-bit masks (one per wave) of the
+// tokens that chose it.  A token's rank for expert e is the number of set
+// bits before it in those masks.
+template <int KMAX>
+__global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
+    const int64_t* __restrict__ topk_idx, int T, int K, int E, int P,
+    uint8_t* __restrict__ is_token_in_partition, bool wide_mask_store,
+    int32_t* __restrict__ pair_code, int32_t* __restrict__ chunk_cnt,
+    int32_t* __restrict__ chunk_pcnt, int32_t* __restrict__ chunk_inv)
+{
+    extern __shared__ unsigned long long lds_bits[];     // [E][kChunkWaves]
+    __shared__ int lds_pcnt[64];
+    __shared__ int lds_inv;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int c = blockIdx.x;
+    const int t = c * kChunk + tid;
+    const int epp = E / P;
+
+    for (int i = tid; i < E * kChunkWaves; i += kChunk)
+        lds_bits[i] = 0ull;
+    if (tid < 64)
+        lds_pcnt[tid] = 0;
+    if (tid == 0)
+        lds_inv = 0;
+    __syncthreads();
+
+    int ids[KMAX];
+    unsigned long long pmask = 0ull;
+    int ninv = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        ids[k] = -1;
+        if (k < K && t < T) {
+            int64_t e = topk_idx[(size_t)t * K + k];
+            if (e >= E) {
+                ninv++;
+            } else if (e >= 0) {
+                bool dup = false;
+#pragma unroll
+                for (int j = 0; j < k; ++j)
+                    dup |= (ids[j] == (int)e);
+                if (dup) {
+                    ninv++;
+                } else {
+                    ids[k] = (int)e;
+                    atomicOr(&lds_bits[(int)e * kChunkWaves + wave], 1ull << lane);
+                    pmask |= 1ull << ((int)e / epp);
+                }
+            }
+        }
+    }
+    if (ninv)
+        atomicAdd(&lds_inv, ninv);
+    for (unsigned long long m = pmask; m; m &= m - 1)
+        atomicAdd(&lds_pcnt[__builtin_ctzll(m)], 1);
+    __syncthreads();
+
+    if (t < T) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k < K) {
+                int code = -1;
+                int e = ids[k];
+                if (e >= 0) {
+                    const unsigned long long* b = &lds_bits[e * kChunkWaves];
+                    int r = __popcll(b[wave] & below);
+                    for (int w = 0; w < wave; ++w)
+                        r += __popcll(b[w]);
+                    code = (e << 8) | r;
+                }
+                pair_code[(size_t)t * K + k] = code;
+            }
+        }
+        uint8_t* dst = is_token_in_partition + (size_t)t * P;
+        if (wide_mask_store) {
+            for (int p0 = 0; p0 < P; p0 += 8) {
+                unsigned long long v = 0ull;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v |= (unsigned long long)((pmask >> (p0 + j)) & 1ull) << (8 * j);
+                *reinterpret_cast<unsigned long long*>(dst + p0) = v;
+            }
+        } else {
+            for (int p = 0; p < P; ++p)
+                dst[p] = (uint8_t)((pmask >> p) & 1ull);
+        }
+    }
+
+    for (int e = tid; e < E; e += kChunk) {
+        int n = 0;
+#pragma unroll
+        for (int w = 0; w < kChunkWaves; ++w)
+            n += __popcll(lds_bits[e * kChunkWaves + w]);
+        chunk_cnt[(size_t)c * E + e] = n;
+    }
+    if (tid < P)
+        chunk_pcnt[(size_t)c * P + tid] = lds_pcnt[tid];
+    if (tid == 0)
+        chunk_inv[c] = lds_inv;
+}
+
+constexpr int kScanThreads = 1024;
+
+// Inclusive sum over the 1024 threads of the block; returns the thread's
+// inclusive prefix and leaves the block total in *total.
+__device__ int block_inclusive_scan(int v, int* lds_wave, int* total)
+{
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int o = __shfl_up(v, d);
+        if (lane >= d)
+            v += o;
+    }
+    if (lane == kWave - 1)
+        lds_wave[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        int s = lane < kScanThreads / kWave ? lds_wave[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kScanThreads / kWave; d <<= 1) {
+            int o = __shfl_up(s, d);
+            if (lane >= d)
+                s += o;
+        }
+        if (lane < kScanThreads / kWave)
+            lds_wave[lane] = s;
+    }
+    __syncthreads();
+    int add = wave > 0 ? lds_wave[wave - 1] : 0;
+    *total = lds_wave[kScanThreads / kWave - 1];
+    __syncthreads();
+    return v + add;
+}
+
+// Column sums of a [B][W] int32 matrix (W <= 1024) with the whole block:
+// thread (col, seg) covers a contiguous run of rows.  When `prefix` is set the
+// matrix is rewritten in place with each column's exclusive running sum.
+// Returns the column total in lds_tot[col].
+__device__ void column_scan(int32_t* __restrict__ m, int B, int W, bool prefix,
+                            int* lds_seg, int* lds_tot)
+{
+    const int tid = threadIdx.x;
+    const int S = kScanThreads / W;               // segments per column
+    const int col = tid % W;
+    const int seg = tid / W;
+    const bool active = seg < S;
+    const int rows_per = (B + S - 1) / S;
+    const int r0 = min(B, seg * rows_per);
+    const int r1 = min(B, r0 + rows_per);
+    int sum = 0;
+    if (active)
+        for (int r = r0; r < r1; ++r)
+            sum += m[(size_t)r * W + col];
+    if (active)
+        lds_seg[seg * W + col] = sum;
+    __syncthreads();
+    if (active) {
+        int before = 0;
+        for (int s = 0; s < seg; ++s)
+            before += lds_seg[s * W + col];
+        if (prefix) {
+            int run = before;
+            for (int r = r0; r < r1; ++r) {
+                int v = m[(size_t)r * W + col];
+                m[(size_t)r * W + col] = run;
+                run += v;
+            }
+        }
+        if (seg == S - 1)
+            lds_tot[col] = before + sum;
+    }
+    __syncthreads();
+}
+
+// One workgroup: chunk counts -> chunk_base (in place), expert totals ->
+// expert_offset; partition and invalid totals; status words for dispatch.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(
+    int B, int E, int P,
+    int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_pcnt,
+    int32_t* __restrict__ chunk_inv,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ num_tokens_per_expert,
+    int32_t* __restrict__ num_tokens_per_partition, int32_t* __restrict__ num_invalid,
+    int32_t* __restrict__ status)
+{
+    __shared__ int lds_seg[kScanThreads];
+    __shared__ int lds_tot[kScanThreads];
+    __shared__ int lds_wave[kScanThreads / kWave];
+    const int tid = threadIdx.x;
+
+    column_scan(chunk_cnt, B, E, true, lds_seg, lds_tot);
+    int cnt = tid < E ? lds_tot[tid] : 0;
+    int total = 0;
+    int incl = block_inclusive_scan(cnt, lds_wave, &total);
+    if (tid < E) {
+        expert_offset[tid] = incl - cnt;
+        num_tokens_per_expert[tid] = cnt;
+    }
+    if (tid == 0) {
+        expert_offset[E] = total;
+        status[2] = total;
+    }
+    __syncthreads();
+
+    column_scan(chunk_pcnt, B, P, false, lds_seg, lds_tot);
+    if (tid < P)
+        num_tokens_per_partition[tid] = lds_tot[tid];
+    __syncthreads();
+
+    column_scan(chunk_inv, B, 1, false, lds_seg, lds_tot);
+    if (tid == 0) {
+        num_invalid[0] = lds_tot[0];
+        status[0] = 0;
+        status[1] = lds_tot[0];
+        status[3] = 0;
+    }
+}
+
+hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
+                         uint8_t* is_token_in_partition, int32_t* pair_code,
+                         int32_t* chunk_cnt, int32_t* chunk_pcnt, int32_t* chunk_inv,
+                         int32_t* expert_offset, int32_t* num_tokens_per_expert,
+                         int32_t* num_tokens_per_partition, int32_t* num_invalid,
+                         int32_t* status, hipStream_t stream)
+{
+    const int B = (T + kChunk - 1) / kChunk;
+    if (B > 0) {
+        size_t lds = (size_t)E * kChunkWaves * sizeof(unsigned long long);
+        dim3 grid(B), block(kChunk);
+        // 8 partition bytes per 64-bit store when rows start 8-byte aligned
+        const bool wide = (P % 8 == 0) && ((reinterpret_cast<uintptr_t>(is_token_in_partition) & 7) == 0);
+#define EP_LAYOUT(KM)                                                                   \
+        hipLaunchKernelGGL(layout_chunk_kernel<KM>, grid, block, lds, stream, topk_idx, \
+                           T, K, E, P, is_token_in_partition, wide, pair_code,          \
+                           chunk_cnt, chunk_pcnt, chunk_inv)
+        if (K <= 2) EP_LAYOUT(2);
+        else if (K <= 4) EP_LAYOUT(4);
+        else if (K <= 8) EP_LAYOUT(8);
+        else EP_LAYOUT(16);
+#undef EP_LAYOUT
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, B, E, P,
+                       chunk_cnt, chunk_pcnt, chunk_inv, expert_offset,
+                       num_tokens_per_expert, num_tokens_per_partition, num_invalid, status);
+    return hipGetLastError();
+}
+
+}  // namespace moe_ep

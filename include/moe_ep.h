@@ -1,0 +1,207 @@
+/*
+ * moe_ep -- MoE expert-parallel dispatch and combine for one rank's share of
+ * the work, on one AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the interface the DeepEP pages describe: the forward flow
+ * get_dispatch_layout -> dispatch(x, topk_idx, topk_weights) -> expert GEMM ->
+ * combine(y, handle), with backward being the other call (stakiran
+ * github-trend-summarizer, "DeepEP 要約", section 3 "使うときの流れ"); the
+ * handle carries the routing metadata combine needs, per-expert received
+ * counts feed the grouped GEMM, and a cached handle lets a caller skip the
+ * layout step when routing has not changed (GeekNews, "Mẫu sử dụng cho huấn
+ * luyện, prefill và decoding").  Destination partitions stand for the EP ranks
+ * of the pages; here they are logical groups of experts within one GPU's HBM.
+ *
+ * Conventions
+ *  - Every call returns EP_OK (0) or a negative EP_E* code; ep_last_error()
+ *    then holds a message (thread-local).  Arguments are validated before any
+ *    HIP call, so an invalid argument never touches the device.
+ *  - Every device buffer and stream belongs to the caller.  The library never
+ *    allocates device memory and never creates streams or events.
+ *  - Every call enqueues its kernels on `stream` and returns without waiting,
+ *    except ep_handle_recv_counts, which synchronises `stream`.
+ *  - Layouts are row-major.  topk_idx is int64 [T, K]; a negative id means
+ *    "masked", an id >= E or an id repeated earlier in the same row is
+ *    "invalid": both are skipped everywhere, invalid ones are counted.
+ *  - Partition p owns experts [p*E/P, (p+1)*E/P).
+ *  - The receive buffer is expert-contiguous: one row per dispatched (t, k)
+ *    pair, experts in ascending id, and within one expert ascending source
+ *    token, with no padding.  Row order is therefore deterministic.
+ *  - FP8 is OCP E4M3FN (max 448).  Each token is quantised once, per block of
+ *    128 channels: a = max(amax, 2^-64), codes = RNE_satfinite(x * (448 / a)),
+ *    scale = a / 448 (fp32, dequantise as code * scale).
+ *  - combine accumulates in fp32 with one fused multiply-add per dispatched k
+ *    in ascending k from +0.0f, then rounds to BF16 (nearest even).
+ *  - Limits: 1 <= K <= 16, 1 <= E <= 1024, 1 <= P <= 64, E % P == 0,
+ *    0 <= T, T*K < 2^31, 1 <= H <= 32768, H % 8 == 0 (H % 128 == 0 for FP8).
+ *    x, recv_x, y and out must be 16-byte aligned, topk_idx 8-byte, the other
+ *    device arrays 4-byte; the workspace 256-byte aligned.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_OK          0
+#define EP_EINVAL     (-1)   /* invalid argument (nothing was enqueued)         */
+#define EP_EHIP       (-2)   /* a HIP runtime call failed                        */
+#define EP_ECAPACITY  (-3)   /* dispatch dropped pairs: capacity_rows < N         */
+#define EP_EIDS       (-4)   /* topk_idx held out-of-range or repeated ids        */
+
+#define EP_MAX_TOPK        16
+#define EP_MAX_EXPERTS     1024
+#define EP_MAX_PARTITIONS  64
+#define EP_MAX_HIDDEN      32768
+
+#define EP_HANDLE_MAGIC    0x31485045u   /* "EPH1" */
+
+/*
+ * Routing metadata of one dispatch, filled by ep_get_dispatch_layout and
+ * completed by ep_dispatch.  A host-side plain struct owned by the caller; the
+ * device arrays it points to live inside the caller's workspace and stay valid
+ * while that workspace is neither freed nor reused by another layout call.
+ * Treat the fields as read-only.
+ */
+typedef struct ep_handle {
+    uint32_t magic;            /* EP_HANDLE_MAGIC once the layout call filled it  */
+    int32_t  stage;            /* 1: layout done, 2: dispatched                    */
+    int32_t  num_tokens;       /* T */
+    int32_t  num_topk;         /* K */
+    int32_t  num_experts;      /* E */
+    int32_t  num_partitions;   /* P */
+    int32_t  hidden;           /* H (set by ep_dispatch)                           */
+    int32_t  use_fp8;          /* 0: BF16 rows, 1: E4M3FN rows + fp32 scales       */
+    int32_t  capacity_rows;    /* rows available in recv_x (set by ep_dispatch)    */
+    int32_t  has_weights;      /* 1 when ep_dispatch copied topk_weights            */
+    int32_t  num_chunks;       /* ceil(T / 256)                                    */
+    int32_t  reserved;
+    void*    ws;               /* the workspace                                    */
+    size_t   ws_bytes;
+    int32_t* expert_offset;    /* [E+1] first receive row of each expert; [E] = N  */
+    int32_t* slot;             /* [T*K] receive row of pair (t,k), -1 if none      */
+    int32_t* src_token;        /* [T*K] source token of receive row r, r < min(N, capacity) */
+    float*   weights;          /* [T*K] copy of topk_weights                       */
+    int32_t* status;           /* [4] overflow flag, num_invalid, N, 0             */
+    int32_t* pair_code;        /* [T*K] (expert << 8 | rank in chunk), -1 if none  */
+    int32_t* chunk_base;       /* [chunks*E] rows of expert e in earlier chunks    */
+    int32_t* chunk_pcnt;       /* [chunks*P] */
+    int32_t* chunk_inv;        /* [chunks]   */
+} ep_handle_t;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int ep_version(void);
+
+/* Message describing the last error returned on this thread ("" if none). */
+const char* ep_last_error(void);
+
+/*
+ * Bytes of device workspace that ep_get_dispatch_layout / ep_dispatch need for
+ * T tokens, top-K, E experts and P partitions (0 on invalid dimensions).  The
+ * workspace holds the handle's arrays and per-chunk tables.
+ */
+size_t ep_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_partitions);
+
+/*
+ * get_dispatch_layout: per-expert and per-partition token counts and the
+ * token-in-partition mask (stakiran summary section 3: get_dispatch_layout
+ * comes before dispatch; devtrends.ru "Как это выглядит в коде": dispatch
+ * takes num_tokens_per_rank).  Also prepares the handle for ep_dispatch.
+ *
+ *   topk_idx                  device int64 [T*K]
+ *   num_tokens_per_partition  device int32 [P]  distinct tokens with >= 1
+ *                             dispatched pair in the partition
+ *   num_tokens_per_expert     device int32 [E]  dispatched pairs per expert
+ *   is_token_in_partition     device uint8 [T*P] 1 if the token has a
+ *                             dispatched pair in the partition, else 0
+ *   num_invalid               device int32 [1]  out-of-range + repeated ids
+ *   ws, ws_bytes              device workspace of ep_workspace_bytes(T,K,E,P)
+ *   handle                    host; overwritten
+ * Errors: EP_EINVAL (bad dims, pointers, alignment, small workspace), EP_EHIP.
+ */
+int ep_get_dispatch_layout(const int64_t* topk_idx, int num_tokens, int num_topk,
+                           int num_experts, int num_partitions,
+                           int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
+                           uint8_t* is_token_in_partition, int32_t* num_invalid,
+                           void* ws, size_t ws_bytes, ep_handle_t* handle,
+                           hipStream_t stream);
+
+/*
+ * dispatch: every dispatched (t, k) pair gets one receive row (the slot scan),
+ * and token t's row is written to each of its rows -- as BF16, or quantised
+ * once to FP8 E4M3FN with per-128-channel fp32 scales (GeekNews usage section:
+ * BF16 and FP8 input; aikraft.ru "Технические детали и требования": FP8
+ * dispatch, BF16 combine).  Must follow ep_get_dispatch_layout with the same
+ * handle on the same stream (or after it completed).
+ *
+ *   x              device bf16 [T*H]
+ *   topk_weights   device fp32 [T*K] or NULL; copied into the workspace for
+ *                  ep_combine, so the caller may free it afterwards
+ *   hidden         H
+ *   use_fp8        0: recv_x is bf16 [capacity_rows*H]; 1: recv_x is
+ *                  e4m3fn bytes [capacity_rows*H], recv_scales fp32
+ *                  [capacity_rows*H/128]
+ *   capacity_rows  rows in recv_x; T*K never overflows, or pass the exact N
+ *                  read back by ep_handle_recv_counts.  Pairs whose row would
+ *                  be >= capacity_rows are dropped (slot -1) and flagged.
+ *   handle         in: from the layout call; out: stage 2
+ * Receive rows at and beyond N are not written.
+ * Errors: EP_EINVAL, EP_EHIP.  Overflow is reported by ep_handle_recv_counts.
+ */
+int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp8,
+                void* recv_x, float* recv_scales, int capacity_rows,
+                ep_handle_t* handle, hipStream_t stream);
+
+/*
+ * Cached dispatch: re-sends new token rows along the routing of an earlier
+ * dispatch, skipping the layout and the slot scan (GeekNews usage section:
+ * routing metadata reused through cached_handle when gating is unchanged).
+ * Output is bit-identical to a fresh ep_dispatch of the same x.
+ *   x, recv_x, recv_scales as in ep_dispatch (same H, use_fp8, capacity).
+ * Errors: EP_EINVAL (handle not dispatched), EP_EHIP.
+ */
+int ep_dispatch_cached(const void* x, const ep_handle_t* handle,
+                       void* recv_x, float* recv_scales, hipStream_t stream);
+
+/*
+ * combine: out[t] = bf16_rne( sum over dispatched k, ascending, of
+ * w[t,k] * y[slot[t,k]] ) with fp32 fused multiply-adds from +0.0f; a token
+ * with no dispatched pair gets a +0 row (GeekNews usage section: combine
+ * reduces expert outputs back to their origin; stakiran section 3).
+ *
+ *   y             device bf16 [rows*H], rows in the receive order of dispatch
+ *   handle        a dispatched handle
+ *   topk_weights  device fp32 [T*K], or NULL to use the copy dispatch took
+ *   out           device bf16 [T*H]
+ * Errors: EP_EINVAL (no weights available, bad pointers), EP_EHIP.
+ */
+int ep_combine(const void* y, const ep_handle_t* handle, const float* topk_weights,
+               void* out, hipStream_t stream);
+
+/*
+ * Per-expert received counts to the host, for the grouped GEMM (GeekNews
+ * usage section: handle.num_recv_tokens_per_expert_list).  Synchronises
+ * `stream`.  host_counts: int32 [E] or NULL; host_num_recv: int32 [1] or NULL
+ * receives N.  Returns EP_ECAPACITY if dispatch dropped pairs, else EP_EIDS if
+ * topk_idx held invalid ids (the counts are valid in both cases), else EP_OK.
+ */
+int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts,
+                          int32_t* host_num_recv, hipStream_t stream);
+
+/*
+ * The device E4M3FN encoder that dispatch uses, applied elementwise:
+ * out[i] = RNE_satfinite_e4m3fn(in[i]) (sign of zero kept).  For testing the
+ * codec on its own.  in: device fp32 [n]; out: device uint8 [n].
+ */
+int ep_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_EP_H */

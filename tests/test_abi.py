@@ -1,0 +1,165 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+the header declares, its struct layout matches the binding, and invalid
+arguments are rejected before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_get_dispatch_scan_amd as ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ep.load()
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in ep._SIGS, f"binding lacks {n}"
+        assert callable(getattr(ep, n)), n
+
+
+def test_handle_layout_matches_c(tmp_path):
+    fields = [f for f, _ in ep.ep_handle_t._fields_]
+    prog = "#include <stdio.h>\n#include <stddef.h>\n#include \"moe_ep.h\"\nint main(void){\n"
+    prog += 'printf("%zu\\n", sizeof(ep_handle_t));\n'
+    for f in fields:
+        prog += f'printf("%zu\\n", offsetof(ep_handle_t, {f}));\n'
+    prog += "return 0;}\n"
+    c = tmp_path / "layout.c"
+    c.write_text(prog)
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(c), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(ep.ep_handle_t)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(ep.ep_handle_t, f).offset == off, f
+
+
+def test_version_and_workspace_size():
+    assert ep.ep_version() >= 10000
+    assert ep.ep_workspace_bytes(0, 8, 256, 8) > 0
+    a = ep.ep_workspace_bytes(8192, 8, 256, 8)
+    b = ep.ep_workspace_bytes(16384, 8, 256, 16)
+    assert b > a > 0
+    # at least slot + src_token + weights + pair codes
+    assert a >= 4 * 8192 * 8 * 4
+    for bad in [(-1, 8, 256, 8), (10, 0, 256, 8), (10, 17, 256, 8), (10, 8, 0, 1),
+                (10, 8, 1025, 1), (10, 8, 256, 7), (10, 8, 256, 128), (1 << 28, 16, 64, 8)]:
+        assert ep.ep_workspace_bytes(*bad) == 0, bad
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails validation first
+
+
+def _layout_args(**kw):
+    a = dict(topk_idx=FAKE, num_tokens=64, num_topk=4, num_experts=16, num_partitions=4,
+             num_tokens_per_partition=FAKE, num_tokens_per_expert=FAKE,
+             is_token_in_partition=FAKE, num_invalid=FAKE, ws=FAKE,
+             ws_bytes=ep.ep_workspace_bytes(64, 4, 16, 4), handle=ep.ep_handle_t(), stream=None)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(num_partitions=3), "invalid dims"),
+    (dict(num_topk=17), "invalid dims"),
+    (dict(num_experts=2048, num_partitions=8), "invalid dims"),
+    (dict(num_tokens=-5), "invalid dims"),
+    (dict(topk_idx=None), "topk_idx"),
+    (dict(topk_idx=FAKE + 4), "topk_idx"),
+    (dict(is_token_in_partition=None), "is_token_in_partition"),
+    (dict(num_invalid=None), "count outputs"),
+    (dict(num_tokens_per_expert=FAKE + 2), "count outputs"),
+    (dict(ws=None), "workspace"),
+    (dict(ws=FAKE + 64), "workspace"),
+    (dict(ws_bytes=100), "workspace too small"),
+])
+def test_layout_rejects_invalid_arguments(kw, msg):
+    a = _layout_args(**kw)
+    rc = ep.ep_get_dispatch_layout(**a)
+    assert rc == ep.EP_EINVAL
+    assert msg in ep.ep_last_error()
+    assert a["handle"].magic == 0
+
+
+def test_layout_rejects_null_handle():
+    a = _layout_args()
+    lib = ep.load()
+    rc = lib.ep_get_dispatch_layout(a["topk_idx"], 64, 4, 16, 4, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    a["ws_bytes"], None, None)
+    assert rc == ep.EP_EINVAL and "handle" in ep.ep_last_error()
+
+
+def _fake_handle(stage=1, T=64, K=4, E=16, P=4):
+    h = ep.ep_handle_t()
+    h.magic = ep.EP_HANDLE_MAGIC
+    h.stage = stage
+    h.num_tokens, h.num_topk, h.num_experts, h.num_partitions = T, K, E, P
+    h.hidden, h.use_fp8, h.capacity_rows = 256, 1, T * K
+    return h
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(hidden=0), "hidden"),
+    (dict(hidden=100), "hidden"),
+    (dict(hidden=65536), "hidden"),
+    (dict(hidden=136, use_fp8=1), "hidden % 128"),
+    (dict(use_fp8=2), "use_fp8"),
+    (dict(capacity_rows=-1), "capacity_rows"),
+    (dict(capacity_rows=64 * 4 + 1), "capacity_rows"),
+    (dict(x=None), "x must"),
+    (dict(x=FAKE + 8), "x must"),
+    (dict(recv_x=FAKE + 4), "recv_x"),
+    (dict(recv_scales=None), "recv_scales"),
+    (dict(topk_weights=FAKE + 2), "topk_weights"),
+])
+def test_dispatch_rejects_invalid_arguments(kw, msg):
+    a = dict(x=FAKE, topk_weights=FAKE, hidden=256, use_fp8=1, recv_x=FAKE, recv_scales=FAKE,
+             capacity_rows=64 * 4, handle=_fake_handle(), stream=None)
+    a.update(kw)
+    rc = ep.ep_dispatch(**a)
+    assert rc == ep.EP_EINVAL, ep.ep_last_error()
+    assert msg in ep.ep_last_error()
+    assert a["handle"].stage == 1
+
+
+def test_calls_need_the_right_stage():
+    h = ep.ep_handle_t()
+    assert ep.ep_dispatch(FAKE, FAKE, 256, 0, FAKE, None, 10, h, None) == ep.EP_EINVAL
+    assert "ep_get_dispatch_layout" in ep.ep_last_error()
+    h1 = _fake_handle(stage=1)
+    assert ep.ep_dispatch_cached(FAKE, h1, FAKE, FAKE, None) == ep.EP_EINVAL
+    assert "dispatched" in ep.ep_last_error()
+    assert ep.ep_combine(FAKE, h1, FAKE, FAKE, None) == ep.EP_EINVAL
+    h2 = _fake_handle(stage=2)
+    h2.has_weights = 0
+    assert ep.ep_combine(FAKE, h2, None, FAKE, None) == ep.EP_EINVAL
+    assert "no weights" in ep.ep_last_error()
+    assert ep.ep_combine(FAKE + 8, h2, FAKE, FAKE, None) == ep.EP_EINVAL
+    assert ep.ep_combine(FAKE, h2, FAKE, FAKE + 8, None) == ep.EP_EINVAL
+    assert ep.ep_handle_recv_counts(ep.ep_handle_t(), None, None, None) == ep.EP_EINVAL
+    assert ep.ep_e4m3fn_encode(None, None, -1, None) == ep.EP_EINVAL
+    assert ep.ep_e4m3fn_encode(None, FAKE, 10, None) == ep.EP_EINVAL
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "combine_get_dispatch_scan_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.lower(), f

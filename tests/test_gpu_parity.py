@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Bit-exact for the layout outputs, slots, source tokens, FP8 codes, scales and
+BF16 rows; combine within 1 BF16 ulp (and expected bit-exact, since both
+sides run the same fp32 fma chain).  Full-size cases run the five workloads
+in the launch configuration the benchmark uses."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _bf16_tensor(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _ulp_diff(a_bits, b_bits):
+    """Distance in BF16 ulps (ordered-integer mapping, +0 == -0)."""
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def run_gpu(ep, idx, w, x, y, E, P, use_fp8, capacity=None, guard_rows=3, pass_weights=True,
+            combine_weights=None):
+    """layout -> dispatch -> counts -> combine on the GPU; returns numpy."""
+    dev = _dev()
+    T, K = idx.shape
+    H = x.shape[1]
+    cap = T * K if capacity is None else capacity
+    t_idx = torch.from_numpy(idx).to(dev)
+    t_w = torch.from_numpy(w).to(dev)
+    t_x = _bf16_tensor(x, dev)
+    lay = ep.get_dispatch_layout(t_idx, E, P)
+    # receive buffers with guard rows filled with a canary pattern
+    if use_fp8:
+        recv_full = torch.full((cap + guard_rows, H), 0xA5, dtype=torch.uint8, device=dev)
+        sc_full = torch.full((cap + guard_rows, H // 128), -7.0, dtype=torch.float32, device=dev)
+        recv = recv_full[:cap].view(torch.float8_e4m3fn)
+        sc = sc_full[:cap]
+    else:
+        recv_full = torch.full((cap + guard_rows, H), 0x5A5A, dtype=torch.int16, device=dev)
+        sc_full = None
+        recv = recv_full[:cap].view(torch.bfloat16)
+        sc = None
+    h = lay.handle
+    rc = ep.ep_dispatch(t_x.data_ptr(), t_w.data_ptr() if pass_weights else None, H, int(use_fp8),
+                        recv.data_ptr(), sc.data_ptr() if sc is not None else None, cap, h.c,
+                        ep._stream())
+    assert rc == ep.EP_OK, ep.ep_last_error()
+    counts, n, status = ep.handle_recv_counts(h)
+    res = dict(
+        num_tokens_per_partition=lay.num_tokens_per_partition.cpu().numpy(),
+        num_tokens_per_expert=lay.num_tokens_per_expert.cpu().numpy(),
+        is_token_in_partition=lay.is_token_in_partition.cpu().numpy(),
+        num_invalid=int(lay.num_invalid.cpu().numpy()[0]),
+        counts=np.array(counts, np.int32), N=n, status=status,
+        slot=h.slot.cpu().numpy(), expert_offset=h.expert_offset.cpu().numpy(),
+        src_token=h.src_token.cpu().numpy(), handle=h, lay=lay,
+        recv_full=recv_full.cpu().numpy(), sc_full=None if sc_full is None else sc_full.cpu().numpy(),
+    )
+    if y is not None:
+        t_y = _bf16_tensor(y, dev) if y.shape[0] > 0 else torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+        cw = None if combine_weights is None else torch.from_numpy(combine_weights).to(dev)
+        out = torch.full((T, H), 0x7777, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        ep.combine(t_y, h, topk_weights=cw, out=out)
+        res["out"] = _bits(out)
+    torch.cuda.synchronize()
+    return res
+
+
+def check(ep, idx, w, x, E, P, use_fp8, capacity=None, y=None, with_combine=True, tag=""):
+    T, K = idx.shape
+    H = x.shape[1]
+    print(f"[parity] {tag} T={T} H={H} E={E} K={K} P={P} fp8={use_fp8} cap={capacity}", flush=True)
+    ref = oracle.run_all(idx, w, x, E, P, use_fp8, capacity=capacity)
+    rows = ref["rows"]
+    if with_combine and y is None:
+        y = workloads.random_rows(T * 31 + H, rows, H, "normal")
+    got = run_gpu(ep, idx, w, x, y if with_combine else None, E, P, use_fp8, capacity=capacity)
+    for key in ("num_tokens_per_partition", "num_tokens_per_expert", "is_token_in_partition"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert got["num_invalid"] == ref["num_invalid"]
+    assert np.array_equal(got["counts"], ref["num_tokens_per_expert"])
+    assert got["N"] == ref["N"]
+    assert np.array_equal(got["expert_offset"], ref["expert_offset"])
+    assert np.array_equal(got["slot"], ref["slot"])
+    assert np.array_equal(got["src_token"][:rows], ref["src_token"])
+    exp_status = ep.EP_ECAPACITY if ref["overflow"] else (ep.EP_EIDS if ref["num_invalid"] else ep.EP_OK)
+    assert got["status"] == exp_status
+    cap = T * K if capacity is None else capacity
+    recv_full = got["recv_full"]
+    if use_fp8:
+        assert np.array_equal(recv_full[:rows], ref["recv_x"])
+        assert np.array_equal(got["sc_full"][:rows].view(np.uint32), ref["recv_scales"].view(np.uint32))
+        # rows past N and the guard rows are never written
+        assert np.all(recv_full[rows:] == 0xA5)
+        assert np.all(got["sc_full"][rows:] == -7.0)
+    else:
+        assert np.array_equal(recv_full[:rows].view(np.uint16), ref["recv_x"])
+        assert np.all(recv_full[rows:] == 0x5A5A)
+    if with_combine:
+        ref_out = oracle.combine(y, ref["slot"], w)
+        d = _ulp_diff(got["out"], ref_out)
+        assert d.max(initial=0) <= 1, f"combine max ulp {d.max()}"
+        assert np.array_equal(got["out"], ref_out), f"combine: {(d > 0).sum()} elements differ by 1 ulp"
+    return ref, got
+
+
+# ----------------------------------------------------------------------------
+# the five workloads at full size
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "skewed", "v3", "large"])
+def test_workload_full_size(ep, name):
+    wl = workloads.config(name)
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    y = workloads.expert_outputs(wl, N)
+    check(ep, idx, w, x, wl.E, wl.P, wl.use_fp8, y=y, tag=name)
+
+
+# ----------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------
+
+SHAPES = [
+    # T, H, E, K, P, fp8
+    (1, 128, 1, 1, 1, True),
+    (1, 8, 4, 2, 2, False),
+    (63, 24, 8, 3, 2, False),
+    (257, 520, 16, 4, 4, False),
+    (300, 1152, 32, 6, 8, True),
+    (513, 2176, 64, 8, 16, True),
+    (700, 256, 1024, 16, 64, True),
+    (1000, 384, 5, 5, 5, True),
+    (2049, 4096, 256, 8, 8, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "T%d_H%d_E%d_K%d_P%d_%s" % (*s[:5], "fp8" if s[5] else "bf16"))
+@pytest.mark.parametrize("mode", ["clean", "dirty"])
+def test_shapes(ep, shape, mode):
+    T, H, E, K, P, fp8 = shape
+    kw = {} if mode == "clean" else dict(distinct=False, mask_frac=0.1, invalid_frac=0.05, dup_frac=0.1)
+    idx, w = workloads.random_case(T * 7 + H, T, E, K, **kw)
+    x = workloads.random_rows(T + H, T, H, "normal")
+    check(ep, idx, w, x, E, P, fp8, tag=f"shape-{mode}")
+
+
+@pytest.mark.parametrize("kind", ["wide", "bits", "zeros", "subnormal", "ties"])
+def test_fp8_value_mixes(ep, kind):
+    T, H, E, K, P = 130, 1024, 16, 4, 4
+    idx, w = workloads.random_case(5, T, E, K)
+    x = workloads.random_rows(6, T, H, kind)
+    check(ep, idx, w, x, E, P, True, tag=f"fp8-{kind}", with_combine=False)
+
+
+@pytest.mark.parametrize("kind", ["wide", "bits", "subnormal"])
+def test_combine_value_mixes(ep, kind):
+    T, H, E, K, P = 200, 512, 32, 8, 4
+    idx, w = workloads.random_case(8, T, E, K, mask_frac=0.1)
+    x = workloads.random_rows(9, T, H, "normal")
+    N = int((idx >= 0).sum())
+    y = workloads.random_rows(10, N, H, kind)
+    if kind == "bits":
+        # keep sums finite: clear the top exponent bit
+        y = (y & np.uint16(0xBFFF)).astype(np.uint16)
+    check(ep, idx, w, x, E, P, False, y=y, tag=f"combine-{kind}")
+
+
+def test_empty_input(ep):
+    dev = _dev()
+    E, P, K, H = 16, 4, 4, 256
+    idx = np.zeros((0, K), np.int64)
+    t_idx = torch.empty((0, K), dtype=torch.int64, device=dev)
+    lay = ep.get_dispatch_layout(t_idx, E, P)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    w = torch.empty((0, K), dtype=torch.float32, device=dev)
+    recv, sc, h = ep.dispatch(x, w, lay, True)
+    counts, n, st = ep.handle_recv_counts(h)
+    out = ep.combine(torch.empty((0, H), dtype=torch.bfloat16, device=dev), h)
+    torch.cuda.synchronize()
+    assert n == 0 and st == ep.EP_OK and sum(counts) == 0
+    assert lay.num_tokens_per_partition.cpu().sum().item() == 0
+    assert lay.num_invalid.cpu().item() == 0
+    assert out.shape == (0, H) and recv.shape == (0, H)
+    del idx
+
+
+@pytest.mark.parametrize("cap_kind", ["exact", "minus7", "half", "zero"])
+def test_capacity(ep, cap_kind):
+    T, H, E, K, P = 333, 1024, 32, 4, 4
+    idx, w = workloads.random_case(21, T, E, K, mask_frac=0.05)
+    x = workloads.random_rows(22, T, H, "normal")
+    N = int((idx >= 0).sum())
+    cap = dict(exact=N, minus7=N - 7, half=N // 2, zero=0)[cap_kind]
+    for fp8 in (False, True):
+        check(ep, idx, w, x, E, P, fp8, capacity=cap, tag=f"cap-{cap_kind}")
+
+
+def test_all_masked_tokens(ep):
+    T, H, E, K, P = 100, 256, 8, 2, 2
+    idx, w = workloads.random_case(31, T, E, K)
+    idx[::3] = -1
+    x = workloads.random_rows(32, T, H, "normal")
+    ref, got = check(ep, idx, w, x, E, P, False, tag="masked-rows")
+    assert np.all(got["out"][::3] == 0)
+
+
+def test_cached_dispatch_is_bit_identical(ep):
+    dev = _dev()
+    for fp8 in (False, True):
+        T, H, E, K, P = 500, 2048, 64, 6, 8
+        idx, w = workloads.random_case(41, T, E, K, mask_frac=0.05)
+        x1 = workloads.random_rows(42, T, H, "normal")
+        x2 = workloads.random_rows(43, T, H, "wide")
+        lay = ep.get_dispatch_layout(torch.from_numpy(idx).to(dev), E, P)
+        t_w = torch.from_numpy(w).to(dev)
+        recv1, sc1, h = ep.dispatch(_bf16_tensor(x1, dev), t_w, lay, fp8)
+        recv2c, sc2c = ep.dispatch_cached(_bf16_tensor(x2, dev), h)
+        lay2 = ep.get_dispatch_layout(torch.from_numpy(idx).to(dev), E, P)
+        recv2f, sc2f, _ = ep.dispatch(_bf16_tensor(x2, dev), t_w, lay2, fp8)
+        torch.cuda.synchronize()
+        N = int((idx >= 0).sum())
+        a = recv2c[:N].view(torch.uint8).cpu().numpy()
+        b = recv2f[:N].view(torch.uint8).cpu().numpy()
+        assert np.array_equal(a, b)
+        if fp8:
+            assert np.array_equal(sc2c[:N].cpu().numpy(), sc2f[:N].cpu().numpy())
+        ref = oracle.run_all(idx, w, x2, E, P, fp8)
+        if fp8:
+            assert np.array_equal(a, ref["recv_x"])
+        else:
+            assert np.array_equal(a.view(np.uint16), ref["recv_x"])
+
+
+def test_combine_weight_sources(ep):
+    dev = _dev()
+    T, H, E, K, P = 128, 512, 16, 4, 4
+    idx, w = workloads.random_case(51, T, E, K)
+    x = workloads.random_rows(52, T, H, "normal")
+    N = int((idx >= 0).sum())
+    y = workloads.random_rows(53, N, H, "normal")
+    w2 = np.ascontiguousarray(w[:, ::-1])
+    # weights given at combine time override the dispatch copy
+    ref = oracle.run_all(idx, w, x, E, P, False)
+    got = run_gpu(ep, idx, w, x, y, E, P, False, combine_weights=w2)
+    assert np.array_equal(got["out"], oracle.combine(y, ref["slot"], w2))
+    # no weights at dispatch: combine without weights is rejected
+    got = run_gpu(ep, idx, w, x, None, E, P, False, pass_weights=False)
+    h = got["handle"]
+    assert h.c.has_weights == 0
+    rc = ep.ep_combine(_bf16_tensor(y, dev).data_ptr(), h.c, None,
+                       torch.empty((T, H), dtype=torch.bfloat16, device=dev).data_ptr(), ep._stream())
+    assert rc == ep.EP_EINVAL
+
+
+def test_determinism(ep):
+    wl = workloads.config("skewed")
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    y = workloads.expert_outputs(wl, N)
+    first = run_gpu(ep, idx, w, x, y, wl.E, wl.P, wl.use_fp8)
+    for _ in range(3):
+        again = run_gpu(ep, idx, w, x, y, wl.E, wl.P, wl.use_fp8)
+        assert again["N"] == first["N"] == N
+        # src_token rows at and beyond N are never written (workspace contents)
+        assert np.array_equal(first["src_token"][:N], again["src_token"][:N])
+        for key in ("slot", "recv_full", "out", "is_token_in_partition", "expert_offset"):
+            assert np.array_equal(first[key], again[key]), key
+
+
+def test_device_e4m3fn_encoder_exhaustive(ep):
+    """Every fp32 bit pattern in [2^-11, 464] (both signs) and a sample below:
+    the device encoder equals the oracle's."""
+    dev = _dev()
+    lo = int(np.float32(2.0 ** -11).view(np.uint32))
+    hi = int(np.float32(464.0).view(np.uint32))
+    step = 1 << 24
+    for start in range(lo, hi + 1, step):
+        u = np.arange(start, min(start + step, hi + 1), dtype=np.uint32)
+        for sign in (0, 0x80000000):
+            v = (u | np.uint32(sign)).view(np.float32)
+            got = ep.e4m3fn_encode(torch.from_numpy(v).to(dev)).cpu().numpy()
+            ref = oracle.e4m3fn_array(v)
+            bad = np.nonzero(got != ref)[0]
+            assert bad.size == 0, (v[bad[:4]], got[bad[:4]], ref[bad[:4]])
+    rng = np.random.default_rng(1)
+    u = rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]
+    v = u.view(np.float32)
+    got = ep.e4m3fn_encode(torch.from_numpy(v).to(dev)).cpu().numpy()
+    assert np.array_equal(got, oracle.e4m3fn_array(v))
