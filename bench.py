@@ -48,8 +48,6 @@ def parse():
     ap.add_argument("--config", default="v3", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
-    ap.add_argument("--copy-calib", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -67,6 +65,36 @@ def byte_counts(wl, N):
     combine_alg = N * H * 2 + T * H * 2 + T * K * 8
     return dict(dispatch_logical=disp_logical, combine_logical=comb_logical,
                 layout_alg=layout_alg, dispatch_alg=dispatch_alg, combine_alg=combine_alg)
+
+
+KERNEL_SOURCES = {
+    "combine_kernel": ["combine_get_dispatch_scan_amd/csrc/combine.hip",
+                       "combine_get_dispatch_scan_amd/csrc/device.h"],
+    "dispatch_fp8_kernel": ["combine_get_dispatch_scan_amd/csrc/dispatch.hip",
+                            "combine_get_dispatch_scan_amd/csrc/device.h"],
+}
+
+
+def measured_traffic(config, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/<config>_hbm_traffic.md), or None when there is none or
+    the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{config}_hbm_traffic.md")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    text = open(path).read()
+    try:
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(blob)[kernel]
+    except (IndexError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != rec["source_sha"]:
+        return None
+    return int(rec["traffic_bytes"])
 
 
 def cpu_baseline(wl, idx, w, x, y, runs):
@@ -126,18 +154,28 @@ def main():
     sp = ep._stream()
     p = lambda t: None if t is None else t.data_ptr()
 
-    def step(ev=None):
-        if ev is not None:
+    def step(ev=None, dom=None):
+        """One pass of the path.  ev: 4 events around the three calls, or
+        (with dom) 2 events around the dominant call only."""
+        if ev is not None and dom is None:
             ev[0].record(stream)
         rc = ep.ep_get_dispatch_layout(p(t_idx), T, K, E, P, p(ntpp), p(ntpe), p(itip), p(ninv),
                                        p(ws), ws.numel(), h, sp)
-        if ev is not None:
+        if ev is not None and dom is None:
             ev[1].record(stream)
+        if dom == "dispatch":
+            ev[0].record(stream)
         rc |= ep.ep_dispatch(p(t_x), p(t_w), H, int(wl.use_fp8), p(recv), p(scales), cap, h, sp)
-        if ev is not None:
+        if dom == "dispatch":
+            ev[1].record(stream)
+        if ev is not None and dom is None:
             ev[2].record(stream)
+        if dom == "combine":
+            ev[0].record(stream)
         rc |= ep.ep_combine(p(t_y), h, None, p(out), sp)
-        if ev is not None:
+        if dom == "combine":
+            ev[1].record(stream)
+        if ev is not None and dom is None:
             ev[3].record(stream)
         rc |= ep.ep_handle_recv_counts(h, counts, ctypes.byref(nrecv), sp)
         if rc != 0:
@@ -149,38 +187,56 @@ def main():
     torch.cuda.synchronize()
     assert nrecv.value == N, (nrecv.value, N)
 
-    # timed region: exactly K steps, wall clock, synchronised on both sides
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # phase breakdown (untimed): events around every call
+    n_ph = max(5, min(args.steps, 20))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ph)]
+    for i in range(n_ph):
+        step(evs[i])
+    torch.cuda.synchronize()
+    mean = lambda v: sum(v) / len(v)
+    phases = {"layout": mean([e[0].elapsed_time(e[1]) for e in evs]),
+              "dispatch": mean([e[1].elapsed_time(e[2]) for e in evs]),
+              "combine": mean([e[2].elapsed_time(e[3]) for e in evs])}
+    # dominant kernel: the larger of dispatch and combine (one kernel launch each)
+    dom = max(("dispatch", "combine"), key=lambda k: phases[k])
+
+    # timed region: exactly K steps, wall clock, synchronised on both sides;
+    # two events per step bracket the dominant kernel on the launch stream
+    dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(dev_ev[i], dom)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    dom_ms = mean([e[0].elapsed_time(e[1]) for e in dev_ev])
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {dom} {dom_ms * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
 
-    lay_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    disp_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
     bc = byte_counts(wl, N)
-    mean = lambda v: sum(v) / len(v)
-    phases = {"layout": mean(lay_ms), "dispatch": mean(disp_ms), "combine": mean(comb_ms)}
-    # dominant kernel: the call with the largest share of the step (each of
-    # dispatch and combine is a single kernel launch)
-    dom = max(("dispatch", "combine"), key=lambda k: phases[k])
     dom_bytes = bc["dispatch_alg"] if dom == "dispatch" else bc["combine_alg"]
-    dom_gbps = dom_bytes / (phases[dom] * 1e-3) / 1e9
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
     dom_kernel = {"dispatch": "dispatch_fp8_kernel" if wl.use_fp8 else "dispatch_bf16_kernel",
                   "combine": "combine_kernel"}[dom]
 
-    if args.copy_calib:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+    # practical ceilings on this GPU, same run: a plain 1 GiB device copy and fill
+    def rate(fn, nbytes, reps=10):
+        fn()
         torch.cuda.synchronize()
-        del src, dst
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes * reps / (a0.elapsed_time(a1) * 1e-3) / 1e9
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    copy_gbps = rate(lambda: dst.copy_(src), 2 << 30)
+    fill_gbps = rate(lambda: dst.fill_(3), 1 << 30)
+    del src, dst
 
     logical = bc["dispatch_logical"] + bc["combine_logical"]
     value = logical / (ms_per_step * 1e-3) / 1e9
@@ -205,10 +261,11 @@ def main():
             "bound": "hbm", "kernel": dom_kernel,
             "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "bytes_per_launch": dom_bytes, "avg_launch_us": round(phases[dom] * 1e3, 2),
-            "traffic": None,
+            "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
+            "traffic": measured_traffic(args.config, dom_kernel),
         },
         "phases_us": {k: round(v * 1e3, 2) for k, v in phases.items()},
+        "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},
         "logical_GBps": {
             "dispatch": round(bc["dispatch_logical"] / ((phases["layout"] + phases["dispatch"]) * 1e-3) / 1e9, 1),
             "combine": round(bc["combine_logical"] / (phases["combine"] * 1e-3) / 1e9, 1),

@@ -69,11 +69,12 @@ WsLayout ws_layout(int T, int K, int E, int P)
     L.chunk_pcnt = o;    o += up(B * P * 4);
     L.chunk_inv = o;     o += up(B * 4);
     L.pair_code = o;     o += up(TK * 4);
-    L.expert_offset = o; o += up(((size_t)E + 1) * 4);
+    // expert_offset [E+1] and status [4] are adjacent: one copy reads both
+    L.expert_offset = o; o += up(((size_t)E + 1 + 4) * 4);
     L.slot = o;          o += up(TK * 4);
     L.src_token = o;     o += up(TK * 4);
     L.weights = o;       o += up(TK * 4);
-    L.status = o;        o += up(4 * 4);
+    L.status = L.expert_offset + ((size_t)E + 1) * 4;
     L.total = o;
     return L;
 }
@@ -284,12 +285,12 @@ int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts, int32
     if (rc)
         return rc;
     const int E = handle->num_experts;
-    int32_t off[EP_MAX_EXPERTS + 1];
-    int32_t st[4];
-    hipError_t e = hipMemcpyAsync(off, handle->expert_offset, sizeof(int32_t) * (E + 1),
+    // expert_offset [E+1] is followed by the 4 status words in the workspace
+    int32_t buf[EP_MAX_EXPERTS + 1 + 4];
+    const int32_t* off = buf;
+    const int32_t* st = buf + E + 1;
+    hipError_t e = hipMemcpyAsync(buf, handle->expert_offset, sizeof(int32_t) * (E + 1 + 4),
                                   hipMemcpyDeviceToHost, stream);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(st, handle->status, sizeof st, hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess)
         e = hipStreamSynchronize(stream);
     if (e != hipSuccess)

@@ -16,9 +16,30 @@
 
 namespace moe_ep {
 
-constexpr int kCombineWaves = 4;
+#ifndef EP_COMBINE_UNROLL
+#define EP_COMBINE_UNROLL 2
+#endif
+#ifndef EP_COMBINE_MIN_ITEMS
+#define EP_COMBINE_MIN_ITEMS 65536
+#endif
+#ifndef EP_COMBINE_MAX_ITERS
+#define EP_COMBINE_MAX_ITERS 4
+#endif
+#ifndef EP_COMBINE_WAVES
+#define EP_COMBINE_WAVES 4
+#endif
+// Cache hints (measured on MI355X: the gathered rows and the output rows are
+// touched once; non-temporal on both sides is fastest).
+#ifndef EP_COMBINE_NT_LOAD
+#define EP_COMBINE_NT_LOAD 1
+#endif
+#ifndef EP_COMBINE_NT_STORE
+#define EP_COMBINE_NT_STORE 1
+#endif
+
+constexpr int kCombineWaves = EP_COMBINE_WAVES;
 constexpr int kCombineChPerIter = kWave * 8;     // 512 channels per wave step
-constexpr int kCombineUnroll = 2;
+constexpr int kCombineUnroll = EP_COMBINE_UNROLL;
 
 struct CombineArgs {
     const uint16_t* y;
@@ -66,7 +87,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
 #pragma unroll
             for (int k = 0; k < KMAX; ++k)
                 if (sk[k] >= 0 && active)
-                    d[u][k] = load16_nt(a.y + (size_t)sk[k] * H + cb);
+                    d[u][k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk[k] * H + cb);
         }
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
@@ -91,7 +112,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
-                store16_nt(orow + cb, o);
+                store16_hint<EP_COMBINE_NT_STORE>(orow + cb, o);
             }
         }
     }
@@ -111,13 +132,9 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slo
     a.w = w;
     a.out = static_cast<uint16_t*>(out);
     a.iters = (H + kCombineChPerIter - 1) / kCombineChPerIter;
-    const int target_waves = 8192;
-    int want = (target_waves + T - 1) / T;
-    int n = want > a.iters ? a.iters : want;
-    if (n < 1)
-        n = 1;
-    a.iters_per_seg = (a.iters + n - 1) / n;
-    a.nseg = (a.iters + a.iters_per_seg - 1) / a.iters_per_seg;
+    const RowSplit rs = split_rows(T, a.iters, EP_COMBINE_MIN_ITEMS, EP_COMBINE_MAX_ITERS);
+    a.nseg = rs.nseg;
+    a.iters_per_seg = rs.iters_per_seg;
     const long long items = (long long)T * a.nseg;
     dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
     dim3 block(kCombineWaves * kWave);

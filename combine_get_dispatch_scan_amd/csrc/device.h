@@ -14,6 +14,33 @@ constexpr int kQBlock = 128;       // channels per FP8 scale
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Work split of a row-streaming kernel: each token row has `iters` wave
+// steps; a work item (one wave) takes `iters_per_item` consecutive steps of
+// one row.  Rows are split only as far as needed to give the launch at least
+// `min_items` work items, so the last round of waves is short.
+struct RowSplit {
+    int nseg, iters_per_seg;
+};
+
+inline RowSplit split_rows(int T, int iters, int min_items, int max_iters_per_item)
+{
+    int n = 1;
+    if (T > 0) {
+        n = (min_items + T - 1) / T;
+        int need = (iters + max_iters_per_item - 1) / max_iters_per_item;
+        if (n < need)
+            n = need;
+    }
+    if (n > iters)
+        n = iters;
+    if (n < 1)
+        n = 1;
+    RowSplit r;
+    r.iters_per_seg = (iters + n - 1) / n;
+    r.nseg = (iters + r.iters_per_seg - 1) / r.iters_per_seg;
+    return r;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ int readlane(int v, int lane)
@@ -26,16 +53,22 @@ __device__ __forceinline__ float readlane_f(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// 16-byte streaming accesses.  The data of the permute and the gather is
-// touched once, so loads and stores are marked non-temporal.
-__device__ __forceinline__ u32x4 load16_nt(const void* p)
+// 16-byte accesses with an optional non-temporal hint (data touched once).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16_hint(const void* p)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    if (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return *reinterpret_cast<const u32x4*>(p);
 }
 
-__device__ __forceinline__ void store16_nt(void* p, u32x4 v)
+template <bool NT>
+__device__ __forceinline__ void store16_hint(void* p, u32x4 v)
 {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    if (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else
+        *reinterpret_cast<u32x4*>(p) = v;
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p)

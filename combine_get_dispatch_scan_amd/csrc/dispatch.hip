@@ -19,10 +19,37 @@
 
 namespace moe_ep {
 
-constexpr int kDispatchWaves = 4;               // waves per workgroup
-constexpr int kFp8ChPerIter = kWave * 16;       // 1024 channels per wave step
-constexpr int kBf16ChPerIter = kWave * 8;       // 512 channels per wave step
-constexpr int kDispatchUnroll = 4;              // wave steps with loads in flight
+#ifndef EP_DISPATCH_UNROLL
+#define EP_DISPATCH_UNROLL 2
+#endif
+#ifndef EP_DISPATCH_MIN_ITEMS
+#define EP_DISPATCH_MIN_ITEMS 65536
+#endif
+#ifndef EP_DISPATCH_MAX_ITERS
+#define EP_DISPATCH_MAX_ITERS 4
+#endif
+#ifndef EP_DISPATCH_WAVES
+#define EP_DISPATCH_WAVES 4
+#endif
+// Issue the first row loads before the slot prologue (measured 2-3 us slower
+// at the V3 shape, so off).
+#ifndef EP_DISPATCH_LOAD_FIRST
+#define EP_DISPATCH_LOAD_FIRST 0
+#endif
+// Cache hints of the row traffic.  Measured on MI355X at the V3 shape: plain
+// loads of x with non-temporal stores of the received rows is fastest (~98 us
+// against ~125 us with both non-temporal and ~138 us with plain stores).
+#ifndef EP_DISPATCH_NT_LOAD
+#define EP_DISPATCH_NT_LOAD 0
+#endif
+#ifndef EP_DISPATCH_NT_STORE
+#define EP_DISPATCH_NT_STORE 1
+#endif
+
+constexpr int kDispatchWaves = EP_DISPATCH_WAVES;   // waves per workgroup
+constexpr int kFp8ChPerIter = kWave * 16;           // 1024 channels per wave step
+constexpr int kBf16ChPerIter = kWave * 8;           // 512 channels per wave step
+constexpr int kDispatchUnroll = EP_DISPATCH_UNROLL; // wave steps with loads in flight
 
 struct DispatchArgs {
     const uint16_t* x;
@@ -84,12 +111,6 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(Di
     if (t >= a.T)
         return;
     const int lane = lane_id();
-    const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
-    int sk[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        sk[k] = k < a.K ? readlane(s_own, k) : -1;
-
     const int H = a.H;
     const int nb = H / kQBlock;
     const uint16_t* xrow = a.x + (size_t)t * H;
@@ -97,19 +118,34 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(Di
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
 
-    for (int i0 = i_begin; i0 < i_end; i0 += kDispatchUnroll) {
-        u32x4 lo[kDispatchUnroll], hi[kDispatchUnroll];
+    u32x4 lo[kDispatchUnroll], hi[kDispatchUnroll];
+    auto load_steps = [&](int i0) {
 #pragma unroll
         for (int u = 0; u < kDispatchUnroll; ++u) {
             const int cb = (i0 + u) * kFp8ChPerIter + lane * 16;
             if (i0 + u < i_end && cb < H) {
-                lo[u] = load16_nt(xrow + cb);
-                hi[u] = load16_nt(xrow + cb + 8);
+                lo[u] = load16_hint<EP_DISPATCH_NT_LOAD>(xrow + cb);
+                hi[u] = load16_hint<EP_DISPATCH_NT_LOAD>(xrow + cb + 8);
             } else {
                 lo[u] = u32x4{0u, 0u, 0u, 0u};
                 hi[u] = u32x4{0u, 0u, 0u, 0u};
             }
         }
+    };
+    // the row loads do not depend on the slots and may start first (measured
+    // slightly slower at the V3 shape, so off by default)
+#if EP_DISPATCH_LOAD_FIRST
+    load_steps(i_begin);
+#endif
+    const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
+    int sk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+
+    for (int i0 = i_begin; i0 < i_end; i0 += kDispatchUnroll) {
+        if (i0 != i_begin || !EP_DISPATCH_LOAD_FIRST)
+            load_steps(i0);
 #pragma unroll
         for (int u = 0; u < kDispatchUnroll; ++u) {
             const int cb = (i0 + u) * kFp8ChPerIter + lane * 16;
@@ -146,7 +182,7 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(Di
 #pragma unroll
                 for (int k = 0; k < KMAX; ++k) {
                     if (sk[k] >= 0) {
-                        store16_nt(recv + (size_t)sk[k] * H + cb, q);
+                        store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, q);
                         if ((lane & 7) == 0)
                             a.scales[(size_t)sk[k] * nb + blk] = scale;
                     }
@@ -165,26 +201,35 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_bf16_kernel(D
     if (t >= a.T)
         return;
     const int lane = lane_id();
-    const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
-    int sk[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        sk[k] = k < a.K ? readlane(s_own, k) : -1;
-
     const int H = a.H;
     const uint16_t* xrow = a.x + (size_t)t * H;
     uint16_t* recv = static_cast<uint16_t*>(a.recv);
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
 
-    for (int i0 = i_begin; i0 < i_end; i0 += kDispatchUnroll) {
-        u32x4 d[kDispatchUnroll];
+    u32x4 d[kDispatchUnroll];
+    auto load_steps = [&](int i0) {
 #pragma unroll
         for (int u = 0; u < kDispatchUnroll; ++u) {
             const int cb = (i0 + u) * kBf16ChPerIter + lane * 8;
             if (i0 + u < i_end && cb < H)
-                d[u] = load16_nt(xrow + cb);
+                d[u] = load16_hint<EP_DISPATCH_NT_LOAD>(xrow + cb);
         }
+    };
+    // the row loads do not depend on the slots and may start first (measured
+    // slightly slower at the V3 shape, so off by default)
+#if EP_DISPATCH_LOAD_FIRST
+    load_steps(i_begin);
+#endif
+    const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
+    int sk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+
+    for (int i0 = i_begin; i0 < i_end; i0 += kDispatchUnroll) {
+        if (i0 != i_begin || !EP_DISPATCH_LOAD_FIRST)
+            load_steps(i0);
 #pragma unroll
         for (int u = 0; u < kDispatchUnroll; ++u) {
             const int cb = (i0 + u) * kBf16ChPerIter + lane * 8;
@@ -192,26 +237,10 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_bf16_kernel(D
 #pragma unroll
                 for (int k = 0; k < KMAX; ++k)
                     if (sk[k] >= 0)
-                        store16_nt(recv + (size_t)sk[k] * H + cb, d[u]);
+                        store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, d[u]);
             }
         }
     }
-}
-
-// Segments per token: enough waves to fill the GPU when T is small, one
-// segment (the whole row) when T alone gives enough waves.
-static void split_rows(int T, int iters, int* nseg, int* iters_per_seg)
-{
-    const int target_waves = 8192;
-    int want = T > 0 ? (target_waves + T - 1) / T : 1;
-    int n = want < 1 ? 1 : (want > iters ? iters : want);
-    if (n < 1)
-        n = 1;
-    int per = (iters + n - 1) / n;
-    if (per < 1)
-        per = 1;
-    *iters_per_seg = per;
-    *nseg = (iters + per - 1) / per;
 }
 
 hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
@@ -239,7 +268,9 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
     a.iters = (L.H + ch - 1) / ch;
     if (a.iters < 1)
         a.iters = 1;
-    split_rows(L.T, a.iters, &a.nseg, &a.iters_per_seg);
+    const RowSplit rs = split_rows(L.T, a.iters, EP_DISPATCH_MIN_ITEMS, EP_DISPATCH_MAX_ITERS);
+    a.nseg = rs.nseg;
+    a.iters_per_seg = rs.iters_per_seg;
     const long long items = (long long)L.T * a.nseg;
     dim3 grid((unsigned)((items + kDispatchWaves - 1) / kDispatchWaves));
     dim3 block(kDispatchWaves * kWave);

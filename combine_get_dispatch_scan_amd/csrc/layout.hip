@@ -123,6 +123,7 @@ __global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kMaxColumnSegs = 16;
 
 // Inclusive sum over the 1024 threads of the block; returns the thread's
 // inclusive prefix and leaves the block total in *total.
@@ -158,14 +159,17 @@ __device__ int block_inclusive_scan(int v, int* lds_wave, int* total)
 }
 
 // Column sums of a [B][W] int32 matrix (W <= 1024) with the whole block:
-// thread (col, seg) covers a contiguous run of rows.  When `prefix` is set the
+// thread (col, seg) covers a contiguous run of rows, with at most
+// kMaxColumnSegs segments per column so the carry-in sum stays short.  When `prefix` is set the
 // matrix is rewritten in place with each column's exclusive running sum.
-// Returns the column total in lds_tot[col].
-__device__ void column_scan(int32_t* __restrict__ m, int B, int W, bool prefix,
-                            int* lds_seg, int* lds_tot)
+// Returns the column total in lds_tot[col].  `m` is in LDS or in global
+// memory (the kernel inlines one copy per address space).
+template <typename Int>
+__device__ __forceinline__ void column_scan(Int* __restrict__ m, int B, int W, bool prefix,
+                                            int* lds_seg, int* lds_tot)
 {
     const int tid = threadIdx.x;
-    const int S = kScanThreads / W;               // segments per column
+    const int S = min(kMaxColumnSegs, kScanThreads / W);   // segments per column
     const int col = tid % W;
     const int seg = tid / W;
     const bool active = seg < S;
@@ -197,8 +201,14 @@ __device__ void column_scan(int32_t* __restrict__ m, int B, int W, bool prefix,
     __syncthreads();
 }
 
+// Largest per-chunk table set (B * (E + P + 1) ints) staged through LDS.
+constexpr int kScanLdsInts = 16384;
+
 // One workgroup: chunk counts -> chunk_base (in place), expert totals ->
 // expert_offset; partition and invalid totals; status words for dispatch.
+// When the three per-chunk tables fit in LDS they are loaded in one pass of
+// independent loads, scanned in LDS and chunk_base is written back; larger
+// tables are scanned in place in global memory.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int B, int E, int P,
     int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_pcnt,
@@ -207,35 +217,60 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int32_t* __restrict__ num_tokens_per_partition, int32_t* __restrict__ num_invalid,
     int32_t* __restrict__ status)
 {
+    extern __shared__ int lds_tab[];              // [B*E | B*P | B] when staged
     __shared__ int lds_seg[kScanThreads];
     __shared__ int lds_tot[kScanThreads];
     __shared__ int lds_wave[kScanThreads / kWave];
     const int tid = threadIdx.x;
+    const int nE = B * E, nP = B * P;
+    const bool staged = (long long)B * (E + P + 1) <= kScanLdsInts;
 
-    column_scan(chunk_cnt, B, E, true, lds_seg, lds_tot);
-    int cnt = tid < E ? lds_tot[tid] : 0;
+    int cnt;
+    int ptot = 0, itot = 0;
+    if (staged) {
+        int* tE = lds_tab;
+        int* tP = lds_tab + nE;
+        int* tI = tP + nP;
+#pragma unroll 4
+        for (int i = tid; i < nE; i += kScanThreads)
+            tE[i] = chunk_cnt[i];
+        for (int i = tid; i < nP; i += kScanThreads)
+            tP[i] = chunk_pcnt[i];
+        for (int i = tid; i < B; i += kScanThreads)
+            tI[i] = chunk_inv[i];
+        __syncthreads();
+        column_scan(tE, B, E, true, lds_seg, lds_tot);
+        cnt = tid < E ? lds_tot[tid] : 0;
+#pragma unroll 4
+        for (int i = tid; i < nE; i += kScanThreads)
+            chunk_cnt[i] = tE[i];
+        column_scan(tP, B, P, false, lds_seg, lds_tot);
+        ptot = tid < P ? lds_tot[tid] : 0;
+        column_scan(tI, B, 1, false, lds_seg, lds_tot);
+        itot = lds_tot[0];
+    } else {
+        column_scan(chunk_cnt, B, E, true, lds_seg, lds_tot);
+        cnt = tid < E ? lds_tot[tid] : 0;
+        column_scan(chunk_pcnt, B, P, false, lds_seg, lds_tot);
+        ptot = tid < P ? lds_tot[tid] : 0;
+        column_scan(chunk_inv, B, 1, false, lds_seg, lds_tot);
+        itot = lds_tot[0];
+    }
+
     int total = 0;
     int incl = block_inclusive_scan(cnt, lds_wave, &total);
     if (tid < E) {
         expert_offset[tid] = incl - cnt;
         num_tokens_per_expert[tid] = cnt;
     }
+    if (tid < P)
+        num_tokens_per_partition[tid] = ptot;
     if (tid == 0) {
         expert_offset[E] = total;
-        status[2] = total;
-    }
-    __syncthreads();
-
-    column_scan(chunk_pcnt, B, P, false, lds_seg, lds_tot);
-    if (tid < P)
-        num_tokens_per_partition[tid] = lds_tot[tid];
-    __syncthreads();
-
-    column_scan(chunk_inv, B, 1, false, lds_seg, lds_tot);
-    if (tid == 0) {
-        num_invalid[0] = lds_tot[0];
+        num_invalid[0] = itot;
         status[0] = 0;
-        status[1] = lds_tot[0];
+        status[1] = itot;
+        status[2] = total;
         status[3] = 0;
     }
 }
@@ -266,7 +301,9 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
         if (err != hipSuccess)
             return err;
     }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, B, E, P,
+    const bool staged = (long long)B * (E + P + 1) <= kScanLdsInts;
+    const size_t scan_lds = staged ? (size_t)B * (E + P + 1) * sizeof(int) : 0;
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), scan_lds, stream, B, E, P,
                        chunk_cnt, chunk_pcnt, chunk_inv, expert_offset,
                        num_tokens_per_expert, num_tokens_per_partition, num_invalid, status);
     return hipGetLastError();
