@@ -82,6 +82,8 @@ _SIGS = {
     "ep_dispatch_cached": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_combine": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_handle_recv_counts": ([ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_handle_recv_counts_async": ([ctypes.POINTER(ep_handle_t), _P, _P], _I),
+    "ep_recv_counts_decode": ([ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_e4m3fn_encode": ([_P, _P, ctypes.c_int64, _P], _I),
 }
 
@@ -148,6 +150,14 @@ def ep_combine(y, handle, topk_weights, out, stream) -> int:
 
 def ep_handle_recv_counts(handle, host_counts, host_num_recv, stream) -> int:
     return load().ep_handle_recv_counts(ctypes.byref(handle), host_counts, host_num_recv, stream)
+
+
+def ep_handle_recv_counts_async(handle, host_buf, stream) -> int:
+    return load().ep_handle_recv_counts_async(ctypes.byref(handle), host_buf, stream)
+
+
+def ep_recv_counts_decode(handle, host_buf, host_counts, host_num_recv) -> int:
+    return load().ep_recv_counts_decode(ctypes.byref(handle), host_buf, host_counts, host_num_recv)
 
 
 def ep_e4m3fn_encode(inp, out, n, stream) -> int:
@@ -299,6 +309,23 @@ def handle_recv_counts(handle: Handle):
     counts = (ctypes.c_int32 * E)()
     n = ctypes.c_int32(0)
     rc = _check(ep_handle_recv_counts(handle.c, counts, ctypes.byref(n), _stream()),
+                ok=(EP_OK, EP_ECAPACITY, EP_EIDS))
+    return list(counts), int(n.value), rc
+
+
+def handle_recv_counts_async(handle: Handle, host_buf):
+    """Enqueue the count readback into ``host_buf`` (int32 [E+5], pinned CPU
+    tensor) without waiting.  Wait on an event recorded after this call, then
+    call ``recv_counts_decode``."""
+    _check(ep_handle_recv_counts_async(handle.c, host_buf.data_ptr(), _stream()))
+
+
+def recv_counts_decode(handle: Handle, host_buf):
+    """Returns (counts list[E], N, status) from a filled ``host_buf``."""
+    E = handle.c.num_experts
+    counts = (ctypes.c_int32 * E)()
+    n = ctypes.c_int32(0)
+    rc = _check(ep_recv_counts_decode(handle.c, host_buf.data_ptr(), counts, ctypes.byref(n)),
                 ok=(EP_OK, EP_ECAPACITY, EP_EIDS))
     return list(counts), int(n.value), rc
 

@@ -277,24 +277,35 @@ int ep_combine(const void* y, const ep_handle_t* handle, const float* topk_weigh
     return EP_OK;
 }
 
-int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts, int32_t* host_num_recv,
-                          hipStream_t stream)
+int ep_handle_recv_counts_async(const ep_handle_t* handle, int32_t* host_buf, hipStream_t stream)
 {
     g_err.clear();
     int rc = check_handle(handle, 1);
     if (rc)
         return rc;
-    const int E = handle->num_experts;
+    if (!host_buf)
+        return fail(EP_EINVAL, "host_buf is NULL");
     // expert_offset [E+1] is followed by the 4 status words in the workspace
-    int32_t buf[EP_MAX_EXPERTS + 1 + 4];
-    const int32_t* off = buf;
-    const int32_t* st = buf + E + 1;
-    hipError_t e = hipMemcpyAsync(buf, handle->expert_offset, sizeof(int32_t) * (E + 1 + 4),
+    hipError_t e = hipMemcpyAsync(host_buf, handle->expert_offset,
+                                  sizeof(int32_t) * (handle->num_experts + 1 + 4),
                                   hipMemcpyDeviceToHost, stream);
-    if (e == hipSuccess)
-        e = hipStreamSynchronize(stream);
     if (e != hipSuccess)
         return hip_fail(e, "reading counts");
+    return EP_OK;
+}
+
+int ep_recv_counts_decode(const ep_handle_t* handle, const int32_t* host_buf,
+                          int32_t* host_counts, int32_t* host_num_recv)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 1);
+    if (rc)
+        return rc;
+    if (!host_buf)
+        return fail(EP_EINVAL, "host_buf is NULL");
+    const int E = handle->num_experts;
+    const int32_t* off = host_buf;
+    const int32_t* st = host_buf + E + 1;
     if (host_counts)
         for (int i = 0; i < E; ++i)
             host_counts[i] = off[i + 1] - off[i];
@@ -306,6 +317,19 @@ int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts, int32
     if (st[1] > 0)
         return fail(EP_EIDS, "topk_idx held %d out-of-range or repeated ids", st[1]);
     return EP_OK;
+}
+
+int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts, int32_t* host_num_recv,
+                          hipStream_t stream)
+{
+    int32_t buf[EP_MAX_EXPERTS + 1 + 4];
+    int rc = ep_handle_recv_counts_async(handle, buf, stream);
+    if (rc)
+        return rc;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "reading counts");
+    return ep_recv_counts_decode(handle, buf, host_counts, host_num_recv);
 }
 
 int ep_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream)

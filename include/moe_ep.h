@@ -195,6 +195,28 @@ int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts,
                           int32_t* host_num_recv, hipStream_t stream);
 
 /*
+ * Asynchronous form of ep_handle_recv_counts, so the host can wait for the
+ * counts while later work (combine, the next layout) is already queued.
+ * Enqueues one device-to-host copy of the handle's expert offsets and status
+ * words into host_buf and returns without waiting.
+ *   host_buf  int32 [E + 5], caller-owned host memory; page-locked memory
+ *             (hipHostMalloc, torch pin_memory) keeps the copy asynchronous
+ * Once the stream has passed this point (the caller waits on an event
+ * recorded after it, or on the stream), ep_recv_counts_decode gives the same
+ * results and return code as ep_handle_recv_counts.
+ * Errors: EP_EINVAL, EP_EHIP.
+ */
+int ep_handle_recv_counts_async(const ep_handle_t* handle, int32_t* host_buf, hipStream_t stream);
+
+/*
+ * Decodes a buffer filled by ep_handle_recv_counts_async (host only, no HIP
+ * call).  host_counts: int32 [E] or NULL; host_num_recv: int32 [1] or NULL.
+ * Returns EP_OK, EP_ECAPACITY or EP_EIDS as ep_handle_recv_counts does.
+ */
+int ep_recv_counts_decode(const ep_handle_t* handle, const int32_t* host_buf,
+                          int32_t* host_counts, int32_t* host_num_recv);
+
+/*
  * The device E4M3FN encoder that dispatch uses, applied elementwise:
  * out[i] = RNE_satfinite_e4m3fn(in[i]) (sign of zero kept).  For testing the
  * codec on its own.  in: device fp32 [n]; out: device uint8 [n].

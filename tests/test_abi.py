@@ -163,3 +163,27 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.lower(), f
+
+
+def test_recv_counts_decode_on_host():
+    """ep_recv_counts_decode is host-only: counts are offset differences, the
+    status words select the return code."""
+    E = 6
+    h = _fake_handle(stage=2, E=E, P=3)
+    h.capacity_rows = 9
+    off = [0, 3, 4, 5, 7, 7, 9]
+    for status, want in [([0, 0, 9, 0], ep.EP_OK), ([1, 0, 9, 0], ep.EP_ECAPACITY),
+                         ([0, 2, 9, 0], ep.EP_EIDS), ([1, 2, 9, 0], ep.EP_ECAPACITY)]:
+        buf = (ctypes.c_int32 * (E + 5))(*(off + status))
+        counts = (ctypes.c_int32 * E)()
+        n = ctypes.c_int32(-1)
+        rc = ep.ep_recv_counts_decode(h, buf, counts, ctypes.byref(n))
+        assert rc == want, (status, rc)
+        assert list(counts) == [3, 1, 1, 2, 0, 2] and n.value == 9
+    # before dispatch the overflow word is not consulted
+    h1 = _fake_handle(stage=1, E=E, P=3)
+    buf = (ctypes.c_int32 * (E + 5))(*(off + [1, 0, 9, 0]))
+    assert ep.ep_recv_counts_decode(h1, buf, None, None) == ep.EP_OK
+    assert ep.ep_recv_counts_decode(h1, None, None, None) == ep.EP_EINVAL
+    assert ep.ep_handle_recv_counts_async(h1, None, None) == ep.EP_EINVAL
+    assert ep.ep_handle_recv_counts_async(ep.ep_handle_t(), FAKE, None) == ep.EP_EINVAL

@@ -272,6 +272,27 @@ def test_combine_weight_sources(ep):
     assert rc == ep.EP_EINVAL
 
 
+def test_async_counts_match_sync(ep):
+    dev = _dev()
+    wl = workloads.config("skewed")
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    for cap in (wl.T * wl.K, N - 5):
+        lay = ep.get_dispatch_layout(torch.from_numpy(idx).to(dev), wl.E, wl.P)
+        recv, sc, h = ep.dispatch(_bf16_tensor(x, dev), torch.from_numpy(w).to(dev), lay, False,
+                                  capacity_rows=cap)
+        buf = torch.full((wl.E + 5,), -9, dtype=torch.int32, pin_memory=True)
+        ep.handle_recv_counts_async(h, buf)
+        ev = torch.cuda.Event()
+        ev.record()
+        ev.synchronize()
+        a = ep.recv_counts_decode(h, buf)
+        b = ep.handle_recv_counts(h)
+        assert a == b
+        assert a[1] == N and a[2] == (ep.EP_OK if cap >= N else ep.EP_ECAPACITY)
+        assert np.array_equal(np.array(a[0]), np.bincount(idx[idx >= 0], minlength=wl.E))
+
+
 def test_determinism(ep):
     wl = workloads.config("skewed")
     idx, w, x = workloads.make(wl)
