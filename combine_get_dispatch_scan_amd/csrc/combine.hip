@@ -28,16 +28,18 @@ namespace moe_ep {
 #ifndef EP_COMBINE_WAVES
 #define EP_COMBINE_WAVES 4
 #endif
-// Cache hints, measured on MI355X at the V3 shape: non-temporal loads of the
-// gathered rows (touched once) and plain write-back stores of the output
-// (~182 us, against ~186 us with non-temporal stores and ~200 us with plain
-// loads).  The 117 MB of output writes cost far more than their share of
-// bandwidth because they interleave with the 940 MB read stream at the DRAM.
+// Cache policy, measured on MI355X at the V3 shape.  The gathered rows are
+// touched once: non-temporal loads (plain loads cost ~30 us more).  The output
+// rows are written with device-scope (sc1) buffer stores, which write through
+// the XCD's L2: ~176 us, against ~180 us with plain write-back stores and
+// ~182-186 us with non-temporal ones.  The 117 MB of output writes cost far
+// more than their share of bandwidth because they interleave with the 940 MB
+// read stream at the DRAM; the write-through policy spreads them best.
 #ifndef EP_COMBINE_NT_LOAD
 #define EP_COMBINE_NT_LOAD 1
 #endif
-#ifndef EP_COMBINE_NT_STORE
-#define EP_COMBINE_NT_STORE 0
+#ifndef EP_COMBINE_STORE_AUX
+#define EP_COMBINE_STORE_AUX 16
 #endif
 
 constexpr int kCombineWaves = EP_COMBINE_WAVES;
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
     }
 
     const int H = a.H;
-    uint16_t* orow = a.out + (size_t)t * H;
+    // one descriptor per output row keeps the byte offsets small for any T
+    const __amdgpu_buffer_rsrc_t orow = make_rsrc(a.out + (size_t)t * H, H * 2);
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
 
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
-                store16_hint<EP_COMBINE_NT_STORE>(orow + cb, o);
+                buffer_store16<EP_COMBINE_STORE_AUX>(o, orow, cb * 2);
             }
         }
     }

@@ -71,6 +71,21 @@ __device__ __forceinline__ void store16_hint(void* p, u32x4 v)
         *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// Buffer-resource store with an explicit cache policy.  The descriptor covers
+// `bytes` bytes from `base` (gfx9 word 3: 32-bit untyped access); `aux` holds
+// the gfx950 policy bits sc0 = 1, nt = 2, sc1 = 16.  The compiler tracks these
+// like any other store; offsets at or past `bytes` are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+
+template <int AUX>
+__device__ __forceinline__ void buffer_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, AUX);
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p)
 {
     return *reinterpret_cast<const u32x4*>(p);
