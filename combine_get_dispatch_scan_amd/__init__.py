@@ -64,6 +64,7 @@ class ep_handle_t(ctypes.Structure):
         ("chunk_base", ctypes.c_void_p),
         ("chunk_pcnt", ctypes.c_void_p),
         ("chunk_inv", ctypes.c_void_p),
+        ("chunk_cnt", ctypes.c_void_p),
     ]
 
 

@@ -39,8 +39,8 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t chunk_cnt, chunk_pcnt, chunk_inv, pair_code, expert_offset, slot, src_token,
-        weights, status, total;
+    size_t chunk_cnt, chunk_base, chunk_pcnt, chunk_inv, pair_code, expert_offset, slot,
+        src_token, weights, status, total;
 };
 
 bool dims_ok(int T, int K, int E, int P)
@@ -66,6 +66,7 @@ WsLayout ws_layout(int T, int K, int E, int P)
     WsLayout L;
     size_t o = 0;
     L.chunk_cnt = o;     o += up(B * E * 4);
+    L.chunk_base = o;    o += up(B * E * 4);
     L.chunk_pcnt = o;    o += up(B * P * 4);
     L.chunk_inv = o;     o += up(B * 4);
     L.pair_code = o;     o += up(TK * 4);
@@ -149,13 +150,14 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
     h.weights = reinterpret_cast<float*>(w + L.weights);
     h.status = reinterpret_cast<int32_t*>(w + L.status);
     h.pair_code = reinterpret_cast<int32_t*>(w + L.pair_code);
-    h.chunk_base = reinterpret_cast<int32_t*>(w + L.chunk_cnt);
+    h.chunk_cnt = reinterpret_cast<int32_t*>(w + L.chunk_cnt);
+    h.chunk_base = reinterpret_cast<int32_t*>(w + L.chunk_base);
     h.chunk_pcnt = reinterpret_cast<int32_t*>(w + L.chunk_pcnt);
     h.chunk_inv = reinterpret_cast<int32_t*>(w + L.chunk_inv);
 
     hipError_t e = moe_ep::launch_layout(topk_idx, T, K, E, P, is_token_in_partition,
-                                         h.pair_code, h.chunk_base, h.chunk_pcnt, h.chunk_inv,
-                                         h.expert_offset, num_tokens_per_expert,
+                                         h.pair_code, h.chunk_cnt, h.chunk_base, h.chunk_pcnt,
+                                         h.chunk_inv, h.expert_offset, num_tokens_per_expert,
                                          num_tokens_per_partition, num_invalid, h.status, stream);
     if (e != hipSuccess)
         return hip_fail(e, "layout launch");

@@ -9,10 +9,10 @@ namespace moe_ep {
 // get_dispatch_layout: per-chunk count kernel + one-workgroup scan kernel.
 hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
                          uint8_t* is_token_in_partition, int32_t* pair_code,
-                         int32_t* chunk_cnt, int32_t* chunk_pcnt, int32_t* chunk_inv,
-                         int32_t* expert_offset, int32_t* num_tokens_per_expert,
-                         int32_t* num_tokens_per_partition, int32_t* num_invalid,
-                         int32_t* status, hipStream_t stream);
+                         int32_t* chunk_cnt, int32_t* chunk_base, int32_t* chunk_pcnt,
+                         int32_t* chunk_inv, int32_t* expert_offset,
+                         int32_t* num_tokens_per_expert, int32_t* num_tokens_per_partition,
+                         int32_t* num_invalid, int32_t* status, hipStream_t stream);
 
 struct DispatchLaunch {
     const void* x;

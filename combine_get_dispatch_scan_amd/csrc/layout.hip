@@ -7,34 +7,36 @@
 // is the exclusive prefix of all earlier pairs of the same expert in token
 // order.  It is split as
 //     slot = expert_offset[e] + chunk_base[c][e] + rank_in_chunk
-// where c is the pair's 256-token chunk.  layout_chunk_kernel computes the
-// rank and the per-chunk counts with lane bitmaps in LDS (no global atomics,
-// so the result does not depend on scheduling); scan_kernel turns the counts
-// into chunk_base and expert_offset.
+// where c is the pair's 256-token chunk.  The counting step computes the rank
+// and the per-chunk counts with lane bitmaps in LDS (no global atomics, so the
+// result does not depend on scheduling); the scan turns the counts into
+// chunk_base and expert_offset.
+//
+// layout_chunk_kernel counts, then the one-workgroup scan_kernel scans.  (A
+// single cooperative launch with a grid barrier in between was measured
+// slower on MI355X: ~22 us for the kernel plus longer launch gaps, against
+// 7 + 7 us for the pair.)
 #include "device.h"
 #include "launch.h"
 
 namespace moe_ep {
 
-// One workgroup of 256 threads per chunk of 256 tokens; thread i owns token
-// c*256 + i.  LDS holds, per expert, four 64-bit masks (one per wave) of the
-// tokens that chose it.  A token's rank for expert e is the number of set
-// bits before it in those masks.
+// Counting step of chunk c (256 tokens, one per thread of a 256-thread
+// block, one block per chunk).  LDS holds, per expert, four 64-bit masks (one per wave) of the
+// tokens that chose it; a token's rank for expert e is the number of set bits
+// before it in those masks.  Writes the pair codes and token-in-partition
+// bytes of the chunk's tokens and row c of the per-chunk count tables.
 template <int KMAX>
-__global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
-    const int64_t* __restrict__ topk_idx, int T, int K, int E, int P,
+__device__ __forceinline__ void count_chunk(
+    const int64_t* __restrict__ topk_idx, int T, int K, int E, int P, int c,
     uint8_t* __restrict__ is_token_in_partition, bool wide_mask_store,
     int32_t* __restrict__ pair_code, int32_t* __restrict__ chunk_cnt,
-    int32_t* __restrict__ chunk_pcnt, int32_t* __restrict__ chunk_inv)
+    int32_t* __restrict__ chunk_pcnt, int32_t* __restrict__ chunk_inv,
+    unsigned long long* lds_bits, int* lds_pcnt, int* lds_inv)
 {
-    extern __shared__ unsigned long long lds_bits[];     // [E][kChunkWaves]
-    __shared__ int lds_pcnt[64];
-    __shared__ int lds_inv;
-
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
-    const int c = blockIdx.x;
     const int t = c * kChunk + tid;
     const int epp = E / P;
 
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
     if (tid < 64)
         lds_pcnt[tid] = 0;
     if (tid == 0)
-        lds_inv = 0;
+        *lds_inv = 0;
     __syncthreads();
 
     int ids[KMAX];
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
         }
     }
     if (ninv)
-        atomicAdd(&lds_inv, ninv);
+        atomicAdd(lds_inv, ninv);
     for (unsigned long long m = pmask; m; m &= m - 1)
         atomicAdd(&lds_pcnt[__builtin_ctzll(m)], 1);
     __syncthreads();
@@ -119,16 +121,29 @@ __global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
     if (tid < P)
         chunk_pcnt[(size_t)c * P + tid] = lds_pcnt[tid];
     if (tid == 0)
-        chunk_inv[c] = lds_inv;
+        chunk_inv[c] = *lds_inv;
 }
 
-constexpr int kScanThreads = 1024;
-constexpr int kMaxColumnSegs = 16;
+template <int KMAX>
+__global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
+    const int64_t* __restrict__ topk_idx, int T, int K, int E, int P,
+    uint8_t* __restrict__ is_token_in_partition, bool wide_mask_store,
+    int32_t* __restrict__ pair_code, int32_t* __restrict__ chunk_cnt,
+    int32_t* __restrict__ chunk_pcnt, int32_t* __restrict__ chunk_inv)
+{
+    extern __shared__ unsigned long long lds_bits[];     // [E][kChunkWaves]
+    __shared__ int lds_pcnt[64];
+    __shared__ int lds_inv;
+    count_chunk<KMAX>(topk_idx, T, K, E, P, blockIdx.x, is_token_in_partition, wide_mask_store,
+                      pair_code, chunk_cnt, chunk_pcnt, chunk_inv, lds_bits, lds_pcnt, &lds_inv);
+}
 
-// Inclusive sum over the 1024 threads of the block; returns the thread's
+// Inclusive sum over the NT threads of the block; returns the thread's
 // inclusive prefix and leaves the block total in *total.
+template <int NT>
 __device__ int block_inclusive_scan(int v, int* lds_wave, int* total)
 {
+    constexpr int NW = NT / kWave;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
 #pragma unroll
@@ -141,32 +156,36 @@ __device__ int block_inclusive_scan(int v, int* lds_wave, int* total)
         lds_wave[wave] = v;
     __syncthreads();
     if (wave == 0) {
-        int s = lane < kScanThreads / kWave ? lds_wave[lane] : 0;
+        int s = lane < NW ? lds_wave[lane] : 0;
 #pragma unroll
-        for (int d = 1; d < kScanThreads / kWave; d <<= 1) {
+        for (int d = 1; d < NW; d <<= 1) {
             int o = __shfl_up(s, d);
             if (lane >= d)
                 s += o;
         }
-        if (lane < kScanThreads / kWave)
+        if (lane < NW)
             lds_wave[lane] = s;
     }
     __syncthreads();
     int add = wave > 0 ? lds_wave[wave - 1] : 0;
-    *total = lds_wave[kScanThreads / kWave - 1];
+    *total = lds_wave[NW - 1];
     __syncthreads();
     return v + add;
 }
 
+constexpr int kScanThreads = 1024;
+constexpr int kMaxColumnSegs = 16;
+
 // Column sums of a [B][W] int32 matrix (W <= 1024) with the whole block:
 // thread (col, seg) covers a contiguous run of rows, with at most
-// kMaxColumnSegs segments per column so the carry-in sum stays short.  When `prefix` is set the
-// matrix is rewritten in place with each column's exclusive running sum.
-// Returns the column total in lds_tot[col].  `m` is in LDS or in global
-// memory (the kernel inlines one copy per address space).
-template <typename Int>
-__device__ __forceinline__ void column_scan(Int* __restrict__ m, int B, int W, bool prefix,
-                                            int* lds_seg, int* lds_tot)
+// kMaxColumnSegs segments per column so the carry-in sum stays short.  When
+// `out` is not null it receives each column's exclusive running sum (it may
+// be the input itself).  Returns the column total in lds_tot[col].  The
+// matrices are in LDS or in global memory (the kernel inlines one copy per
+// address space).
+template <typename In, typename Out>
+__device__ __forceinline__ void column_scan(const In* m, Out* out, int B, int W, int* lds_seg,
+                                            int* lds_tot)
 {
     const int tid = threadIdx.x;
     const int S = min(kMaxColumnSegs, kScanThreads / W);   // segments per column
@@ -187,11 +206,11 @@ __device__ __forceinline__ void column_scan(Int* __restrict__ m, int B, int W, b
         int before = 0;
         for (int s = 0; s < seg; ++s)
             before += lds_seg[s * W + col];
-        if (prefix) {
+        if (out) {
             int run = before;
             for (int r = r0; r < r1; ++r) {
                 int v = m[(size_t)r * W + col];
-                m[(size_t)r * W + col] = run;
+                out[(size_t)r * W + col] = run;
                 run += v;
             }
         }
@@ -204,15 +223,15 @@ __device__ __forceinline__ void column_scan(Int* __restrict__ m, int B, int W, b
 // Largest per-chunk table set (B * (E + P + 1) ints) staged through LDS.
 constexpr int kScanLdsInts = 16384;
 
-// One workgroup: chunk counts -> chunk_base (in place), expert totals ->
-// expert_offset; partition and invalid totals; status words for dispatch.
-// When the three per-chunk tables fit in LDS they are loaded in one pass of
-// independent loads, scanned in LDS and chunk_base is written back; larger
-// tables are scanned in place in global memory.
+// One workgroup: chunk counts -> chunk_base, expert totals -> expert_offset;
+// partition and invalid totals; status words for dispatch.  When the three
+// per-chunk tables fit in LDS they are loaded in one pass of independent
+// loads, scanned in LDS and chunk_base is written out; larger tables are
+// scanned from global memory.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int B, int E, int P,
-    int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_pcnt,
-    int32_t* __restrict__ chunk_inv,
+    const int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ chunk_pcnt, const int32_t* __restrict__ chunk_inv,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ num_tokens_per_expert,
     int32_t* __restrict__ num_tokens_per_partition, int32_t* __restrict__ num_invalid,
     int32_t* __restrict__ status)
@@ -239,26 +258,26 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
         for (int i = tid; i < B; i += kScanThreads)
             tI[i] = chunk_inv[i];
         __syncthreads();
-        column_scan(tE, B, E, true, lds_seg, lds_tot);
+        column_scan(tE, tE, B, E, lds_seg, lds_tot);
         cnt = tid < E ? lds_tot[tid] : 0;
 #pragma unroll 4
         for (int i = tid; i < nE; i += kScanThreads)
-            chunk_cnt[i] = tE[i];
-        column_scan(tP, B, P, false, lds_seg, lds_tot);
+            chunk_base[i] = tE[i];
+        column_scan(tP, (int*)nullptr, B, P, lds_seg, lds_tot);
         ptot = tid < P ? lds_tot[tid] : 0;
-        column_scan(tI, B, 1, false, lds_seg, lds_tot);
+        column_scan(tI, (int*)nullptr, B, 1, lds_seg, lds_tot);
         itot = lds_tot[0];
     } else {
-        column_scan(chunk_cnt, B, E, true, lds_seg, lds_tot);
+        column_scan(chunk_cnt, chunk_base, B, E, lds_seg, lds_tot);
         cnt = tid < E ? lds_tot[tid] : 0;
-        column_scan(chunk_pcnt, B, P, false, lds_seg, lds_tot);
+        column_scan(chunk_pcnt, (int32_t*)nullptr, B, P, lds_seg, lds_tot);
         ptot = tid < P ? lds_tot[tid] : 0;
-        column_scan(chunk_inv, B, 1, false, lds_seg, lds_tot);
+        column_scan(chunk_inv, (int32_t*)nullptr, B, 1, lds_seg, lds_tot);
         itot = lds_tot[0];
     }
 
     int total = 0;
-    int incl = block_inclusive_scan(cnt, lds_wave, &total);
+    int incl = block_inclusive_scan<kScanThreads>(cnt, lds_wave, &total);
     if (tid < E) {
         expert_offset[tid] = incl - cnt;
         num_tokens_per_expert[tid] = cnt;
@@ -277,17 +296,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
 hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
                          uint8_t* is_token_in_partition, int32_t* pair_code,
-                         int32_t* chunk_cnt, int32_t* chunk_pcnt, int32_t* chunk_inv,
-                         int32_t* expert_offset, int32_t* num_tokens_per_expert,
-                         int32_t* num_tokens_per_partition, int32_t* num_invalid,
-                         int32_t* status, hipStream_t stream)
+                         int32_t* chunk_cnt, int32_t* chunk_base, int32_t* chunk_pcnt,
+                         int32_t* chunk_inv, int32_t* expert_offset,
+                         int32_t* num_tokens_per_expert, int32_t* num_tokens_per_partition,
+                         int32_t* num_invalid, int32_t* status, hipStream_t stream)
 {
     const int B = (T + kChunk - 1) / kChunk;
+    const size_t lds = (size_t)E * kChunkWaves * sizeof(unsigned long long);
+    // 8 partition bytes per 64-bit store when rows start 8-byte aligned
+    const bool wide = (P % 8 == 0) && ((reinterpret_cast<uintptr_t>(is_token_in_partition) & 7) == 0);
     if (B > 0) {
-        size_t lds = (size_t)E * kChunkWaves * sizeof(unsigned long long);
         dim3 grid(B), block(kChunk);
-        // 8 partition bytes per 64-bit store when rows start 8-byte aligned
-        const bool wide = (P % 8 == 0) && ((reinterpret_cast<uintptr_t>(is_token_in_partition) & 7) == 0);
 #define EP_LAYOUT(KM)                                                                   \
         hipLaunchKernelGGL(layout_chunk_kernel<KM>, grid, block, lds, stream, topk_idx, \
                            T, K, E, P, is_token_in_partition, wide, pair_code,          \
@@ -304,7 +323,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
     const bool staged = (long long)B * (E + P + 1) <= kScanLdsInts;
     const size_t scan_lds = staged ? (size_t)B * (E + P + 1) * sizeof(int) : 0;
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), scan_lds, stream, B, E, P,
-                       chunk_cnt, chunk_pcnt, chunk_inv, expert_offset,
+                       chunk_cnt, chunk_base, chunk_pcnt, chunk_inv, expert_offset,
                        num_tokens_per_expert, num_tokens_per_partition, num_invalid, status);
     return hipGetLastError();
 }

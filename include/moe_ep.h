@@ -93,6 +93,7 @@ typedef struct ep_handle {
     int32_t* chunk_base;       /* [chunks*E] rows of expert e in earlier chunks    */
     int32_t* chunk_pcnt;       /* [chunks*P] */
     int32_t* chunk_inv;        /* [chunks]   */
+    int32_t* chunk_cnt;        /* [chunks*E] rows of expert e in each chunk        */
 } ep_handle_t;
 
 /* Library version, major*10000 + minor*100 + patch. */
