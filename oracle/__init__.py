@@ -64,6 +64,10 @@ def lib():
         L.oracle_dispatch.restype = None
         L.oracle_combine.argtypes = [P, i32, i32, i32, P, P, P]
         L.oracle_combine.restype = None
+        L.oracle_dispatch_backward.argtypes = [P, i32, i32, i32, P, P]
+        L.oracle_dispatch_backward.restype = None
+        L.oracle_combine_backward.argtypes = [P, P, i32, i32, i32, P, P, P, P]
+        L.oracle_combine_backward.restype = None
         _lib = L
     return _lib
 
@@ -172,6 +176,34 @@ def combine(y_bits: np.ndarray, slot: np.ndarray, w: np.ndarray) -> np.ndarray:
     out = np.empty((T, H), np.uint16)
     lib().oracle_combine(_p(y), T, H, K, _p(slot), _p(w), _p(out))
     return out
+
+
+def dispatch_backward(grad_recv_bits: np.ndarray, slot: np.ndarray) -> np.ndarray:
+    """grad_x [T,H] bf16 bits from grad_recv [rows,H] bf16 bits."""
+    g = _c(grad_recv_bits, np.uint16)
+    slot = _c(slot, np.int32)
+    T, K = slot.shape
+    H = g.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().oracle_dispatch_backward(_p(g), T, H, K, _p(slot), _p(out))
+    return out
+
+
+def combine_backward(grad_out_bits: np.ndarray, y_bits, slot: np.ndarray, w: np.ndarray,
+                     rows: int, fill: int = 0):
+    """Returns (grad_y [rows,H] bf16 bits, rows nobody maps to = fill;
+    grad_w [T,K] fp32 or None when y_bits is None)."""
+    g = _c(grad_out_bits, np.uint16)
+    slot = _c(slot, np.int32)
+    w = _c(w, np.float32)
+    T, K = slot.shape
+    H = g.shape[1]
+    grad_y = np.full((rows, H), fill, np.uint16)
+    y = None if y_bits is None else _c(y_bits, np.uint16)
+    grad_w = None if y is None else np.empty((T, K), np.float32)
+    lib().oracle_combine_backward(_p(g), None if y is None else _p(y), T, H, K, _p(slot), _p(w),
+                                  _p(grad_y), None if grad_w is None else _p(grad_w))
+    return grad_y, grad_w
 
 
 def run_all(topk_idx, topk_weights, x_bits, E, P, use_fp8, capacity=None, y_bits=None):

@@ -280,3 +280,56 @@ void oracle_combine(const uint16_t* y, int T, int H, int K, const int32_t* slot,
         }
     }
 }
+
+/* Backward of dispatch (straight-through for the FP8 cast): each token's
+ * gradient is the sum of the gradients of its received rows.  The sum is the
+ * combine definition with unit weights: fp32, k ascending, from +0.0f, then
+ * one rounding to BF16. */
+void oracle_dispatch_backward(const uint16_t* grad_recv, int T, int H, int K,
+                              const int32_t* slot, uint16_t* grad_x)
+{
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < H; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int32_t r = slot[(size_t)t * K + k];
+                if (r < 0)
+                    continue;
+                acc = acc + oracle_bf16_to_f32(grad_recv[(size_t)r * H + j]);
+            }
+            grad_x[(size_t)t * H + j] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
+/* Backward of combine.  out[t] = sum_k w[t,k] * y[slot[t,k]] is linear in y
+ * and in w: d out / d y[slot[t,k]] = w[t,k] (so grad_y is grad_out scaled by
+ * the weight and sent back along the pair), and d out / d w[t,k] =
+ * y[slot[t,k]] (so grad_w is a dot product over the hidden dimension).  The
+ * dot product is taken in double and rounded once to fp32. */
+void oracle_combine_backward(const uint16_t* grad_out, const uint16_t* y, int T, int H, int K,
+                             const int32_t* slot, const float* w, uint16_t* grad_y,
+                             float* grad_w)
+{
+    for (int t = 0; t < T; ++t) {
+        const uint16_t* g = grad_out + (size_t)t * H;
+        for (int k = 0; k < K; ++k) {
+            int32_t r = slot[(size_t)t * K + k];
+            if (r < 0) {
+                if (y)
+                    grad_w[(size_t)t * K + k] = 0.0f;
+                continue;
+            }
+            float wk = w[(size_t)t * K + k];
+            for (int j = 0; j < H; ++j)
+                grad_y[(size_t)r * H + j] = oracle_bf16_rne(wk * oracle_bf16_to_f32(g[j]));
+            if (y) {
+                double dot = 0.0;
+                for (int j = 0; j < H; ++j)
+                    dot += (double)oracle_bf16_to_f32(g[j]) *
+                           (double)oracle_bf16_to_f32(y[(size_t)r * H + j]);
+                grad_w[(size_t)t * K + k] = (float)dot;
+            }
+        }
+    }
+}

@@ -74,6 +74,23 @@ void oracle_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* slot
 void oracle_combine(const uint16_t* y, int T, int H, int K, const int32_t* slot,
                     const float* w, uint16_t* out);
 
+/* Backward of dispatch: the backward of dispatch is combine (stakiran summary,
+ * section 3).  With the FP8 cast taken as straight-through, grad_x[t] =
+ * bf16_rne( fp32 sum over dispatched k ascending of grad_recv[slot[t,k]],
+ * from +0.0f ); a token with no dispatched pair gets +0. */
+void oracle_dispatch_backward(const uint16_t* grad_recv, int T, int H, int K,
+                              const int32_t* slot, uint16_t* grad_x);
+
+/* Backward of combine: the backward of combine is dispatch (stakiran summary,
+ * section 3), here of grad_out scaled by each pair's weight:
+ *   grad_y[slot[t,k]][j] = bf16_rne( w[t,k] * grad_out[t][j] )  (one fp32 product)
+ *   grad_w[t,k] = (float) sum_j grad_out[t][j] * y[slot[t,k]][j]  (sum in double)
+ * Rows of grad_y that no pair maps to are left untouched; grad_w is 0 for
+ * pairs that were not dispatched.  y == NULL skips grad_w. */
+void oracle_combine_backward(const uint16_t* grad_out, const uint16_t* y, int T, int H, int K,
+                             const int32_t* slot, const float* w, uint16_t* grad_y,
+                             float* grad_w);
+
 #ifdef __cplusplus
 }
 #endif

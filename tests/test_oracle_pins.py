@@ -477,3 +477,91 @@ def test_workload_invariants(name):
     if name == "skewed":
         c = lay["num_tokens_per_expert"]
         assert c.max() > 20 * max(c.min(), 1)
+
+
+# ----------------------------------------------------------------------------
+# backward calls
+# ----------------------------------------------------------------------------
+
+def _small_int_bf16(rng, shape, lo=-3, hi=4):
+    return workloads.bf16_bits_from_f32(rng.integers(lo, hi, shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("T,E,K,P,H", [(33, 8, 3, 2, 16), (130, 64, 6, 8, 24), (64, 16, 16, 4, 8)])
+def test_dispatch_backward_is_the_adjoint_of_dispatch(T, E, K, P, H):
+    """<dispatch(x), g> == <x, dispatch_backward(g)> exactly on small integers
+    (the backward of dispatch is combine with unit weights)."""
+    rng = np.random.default_rng(T + K)
+    idx, _ = workloads.random_case(T, T, E, K, mask_frac=0.15, distinct=K <= E,
+                                   invalid_frac=0.05)
+    w = np.ones((T, K), np.float32)
+    x = _small_int_bf16(rng, (T, H))
+    r = oracle.run_all(idx, w, x, E, P, False)
+    g = _small_int_bf16(rng, (r["rows"], H))
+    lhs = (_f32(r["recv_x"]).astype(np.float64) * _f32(g)).sum()
+    gx = oracle.dispatch_backward(g, r["slot"])
+    rhs = (_f32(x).astype(np.float64) * _f32(gx)).sum()
+    assert lhs == rhs
+    # a token none of whose pairs was dispatched gets a +0 gradient
+    dead = (r["slot"] < 0).all(axis=1)
+    assert np.all(gx[dead] == 0)
+
+
+@pytest.mark.parametrize("T,E,K,P,H", [(40, 8, 3, 2, 16), (96, 32, 8, 4, 32)])
+def test_combine_backward_grad_y_is_the_adjoint_of_combine(T, E, K, P, H):
+    """<combine_w(y), g> == <y, grad_y> exactly (small integers, weights in
+    {1/2, 1, 2}); rows no pair maps to keep their previous contents."""
+    rng = np.random.default_rng(7 * T + K)
+    idx, _ = workloads.random_case(T + 1, T, E, K, mask_frac=0.2)
+    w = np.array([0.5, 1.0, 2.0], np.float32)[rng.integers(0, 3, (T, K))]
+    r = oracle.run_all(idx, w, None, E, P, False, capacity=T * K)
+    rows = T * K
+    y = _small_int_bf16(rng, (rows, H))
+    g = _small_int_bf16(rng, (T, H))
+    out = oracle.combine(y, r["slot"], w)
+    gy, gw = oracle.combine_backward(g, y, r["slot"], w, rows, fill=0x7777)
+    used = np.zeros(rows, bool)
+    used[r["slot"][r["slot"] >= 0]] = True
+    assert np.all(gy[~used] == 0x7777)
+    gy_f = np.where(used[:, None], _f32(gy).astype(np.float64), 0.0)
+    lhs = (_f32(out).astype(np.float64) * _f32(g)).sum()
+    rhs = (_f32(y).astype(np.float64) * gy_f).sum()
+    assert lhs == rhs
+    assert np.all(gw[r["slot"] < 0] == 0)
+
+
+def test_combine_backward_grad_w_matches_finite_differences():
+    """combine is linear in w: <combine(y, w + e_tk), g> - <combine(y, w), g>
+    equals grad_w[t, k] exactly when every value is a small integer."""
+    rng = np.random.default_rng(3)
+    T, E, K, P, H = 24, 16, 4, 4, 16
+    idx, _ = workloads.random_case(5, T, E, K, mask_frac=0.1)
+    w = rng.integers(1, 3, (T, K)).astype(np.float32)
+    r = oracle.run_all(idx, w, None, E, P, False)
+    y = _small_int_bf16(rng, (r["rows"], H))
+    g = _small_int_bf16(rng, (T, H))
+    _, gw = oracle.combine_backward(g, y, r["slot"], w, r["rows"])
+    base = (_f32(oracle.combine(y, r["slot"], w)).astype(np.float64) * _f32(g)).sum()
+    for t in range(T):
+        for k in range(K):
+            w2 = w.copy()
+            w2[t, k] += 1.0
+            bumped = (_f32(oracle.combine(y, r["slot"], w2)).astype(np.float64) * _f32(g)).sum()
+            assert gw[t, k] == bumped - base, (t, k)
+
+
+def test_combine_backward_grad_y_single_rounding():
+    """grad_y is one fp32 product rounded once to BF16 (checked against
+    torch's multiply and BF16 rounding on wide-range values)."""
+    T, E, K, P, H = 50, 8, 2, 2, 128
+    idx, _ = workloads.random_case(9, T, E, K)
+    w = workloads.random_case(9, T, E, K, weights="dirichlet")[1]
+    r = oracle.run_all(idx, w, None, E, P, False)
+    g = workloads.random_rows(10, T, H, "wide")
+    gy, _ = oracle.combine_backward(g, None, r["slot"], w, r["rows"])
+    gt = torch.from_numpy(_f32(g))
+    for t in range(T):
+        for k in range(K):
+            s = r["slot"][t, k]
+            ref = (gt[t] * torch.tensor(float(w[t, k]), dtype=torch.float32)).to(torch.bfloat16)
+            assert np.array_equal(gy[s], ref.view(torch.int16).numpy().view(np.uint16))
