@@ -10,7 +10,8 @@ Two layers:
 * ``ep_*`` -- one function per C entry point of ``include/moe_ep.h``, same
   names and arguments (device pointers as ints, the stream as a handle).
 * ``get_dispatch_layout`` / ``dispatch`` / ``dispatch_cached`` / ``combine`` /
-  ``handle_recv_counts`` -- the same calls on torch tensors: they allocate
+  ``dispatch_backward`` / ``combine_backward`` / ``handle_recv_counts`` -- the
+  same calls on torch tensors: they allocate
   the outputs with ``torch.empty`` on the tensors' device and launch on torch's
   current stream.
 """
@@ -82,6 +83,8 @@ _SIGS = {
     "ep_dispatch": ([_P, _P, _I, _I, _P, _P, _I, ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_dispatch_cached": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_combine": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_dispatch_backward": ([_P, ctypes.POINTER(ep_handle_t), _P, _P], _I),
+    "ep_combine_backward": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P, _P, _P], _I),
     "ep_handle_recv_counts": ([ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_handle_recv_counts_async": ([ctypes.POINTER(ep_handle_t), _P, _P], _I),
     "ep_recv_counts_decode": ([ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
@@ -147,6 +150,15 @@ def ep_dispatch_cached(x, handle, recv_x, recv_scales, stream) -> int:
 
 def ep_combine(y, handle, topk_weights, out, stream) -> int:
     return load().ep_combine(y, ctypes.byref(handle), topk_weights, out, stream)
+
+
+def ep_dispatch_backward(grad_recv, handle, grad_x, stream) -> int:
+    return load().ep_dispatch_backward(grad_recv, ctypes.byref(handle), grad_x, stream)
+
+
+def ep_combine_backward(grad_out, y, handle, topk_weights, grad_y, grad_w, stream) -> int:
+    return load().ep_combine_backward(grad_out, y, ctypes.byref(handle), topk_weights, grad_y,
+                                      grad_w, stream)
 
 
 def ep_handle_recv_counts(handle, host_counts, host_num_recv, stream) -> int:
@@ -301,6 +313,32 @@ def combine(y, handle: Handle, topk_weights=None, out=None):
         out = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=y.device)
     _check(ep_combine(_ptr(y), c, _ptr(topk_weights), _ptr(out), _stream()))
     return out
+
+
+def dispatch_backward(grad_recv, handle: Handle, grad_x=None):
+    """grad_recv: bf16 [rows, H] in the receive order.  Returns grad_x bf16 [T, H]."""
+    import torch
+    c = handle.c
+    if grad_x is None:
+        grad_x = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=grad_recv.device)
+    _check(ep_dispatch_backward(_ptr(grad_recv), c, _ptr(grad_x), _stream()))
+    return grad_x
+
+
+def combine_backward(grad_out, handle: Handle, y=None, topk_weights=None, grad_y=None):
+    """grad_out: bf16 [T, H].  Returns (grad_y bf16 [capacity, H], grad_w fp32
+    [T, K] or None when y is None).  Rows of grad_y that no pair maps to are
+    left as allocated."""
+    import torch
+    c = handle.c
+    dev = grad_out.device
+    if grad_y is None:
+        grad_y = torch.empty((c.capacity_rows, c.hidden), dtype=torch.bfloat16, device=dev)
+    grad_w = None if y is None else torch.empty((c.num_tokens, c.num_topk), dtype=torch.float32,
+                                                device=dev)
+    _check(ep_combine_backward(_ptr(grad_out), _ptr(y), c, _ptr(topk_weights), _ptr(grad_y),
+                               _ptr(grad_w), _stream()))
+    return grad_y, grad_w
 
 
 def handle_recv_counts(handle: Handle):

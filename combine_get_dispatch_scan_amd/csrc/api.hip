@@ -279,6 +279,56 @@ int ep_combine(const void* y, const ep_handle_t* handle, const float* topk_weigh
     return EP_OK;
 }
 
+int ep_dispatch_backward(const void* grad_recv, const ep_handle_t* handle, void* grad_x,
+                         hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 2);
+    if (rc)
+        return rc;
+    const int T = handle->num_tokens;
+    if (T > 0 && (!grad_x || !aligned(grad_x, 16)))
+        return fail(EP_EINVAL, "grad_x must be a non-NULL 16-byte aligned device pointer");
+    if (T > 0 && handle->capacity_rows > 0 && (!grad_recv || !aligned(grad_recv, 16)))
+        return fail(EP_EINVAL, "grad_recv must be a non-NULL 16-byte aligned device pointer");
+    hipError_t e = moe_ep::launch_combine(grad_recv, T, handle->hidden, handle->num_topk,
+                                          handle->slot, nullptr, grad_x, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "dispatch backward launch");
+    return EP_OK;
+}
+
+int ep_combine_backward(const void* grad_out, const void* y, const ep_handle_t* handle,
+                        const float* topk_weights, void* grad_y, float* grad_w,
+                        hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 2);
+    if (rc)
+        return rc;
+    const int T = handle->num_tokens;
+    const float* w = topk_weights ? topk_weights : (handle->has_weights ? handle->weights : nullptr);
+    if (!w && T > 0)
+        return fail(EP_EINVAL, "no weights: pass topk_weights or give them to ep_dispatch");
+    if (w && !aligned(w, 4))
+        return fail(EP_EINVAL, "topk_weights must be 4-byte aligned");
+    if (T > 0 && (!grad_out || !aligned(grad_out, 16)))
+        return fail(EP_EINVAL, "grad_out must be a non-NULL 16-byte aligned device pointer");
+    const bool rows = T > 0 && handle->capacity_rows > 0;
+    if (rows && (!grad_y || !aligned(grad_y, 16)))
+        return fail(EP_EINVAL, "grad_y must be a non-NULL 16-byte aligned device pointer");
+    if (grad_w && !aligned(grad_w, 4))
+        return fail(EP_EINVAL, "grad_w must be 4-byte aligned");
+    if (grad_w && rows && (!y || !aligned(y, 16)))
+        return fail(EP_EINVAL, "grad_w needs y: a non-NULL 16-byte aligned device pointer");
+    hipError_t e = moe_ep::launch_combine_backward(grad_out, y, T, handle->hidden,
+                                                   handle->num_topk, handle->slot, w, grad_y,
+                                                   grad_w, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "combine backward launch");
+    return EP_OK;
+}
+
 int ep_handle_recv_counts_async(const ep_handle_t* handle, int32_t* host_buf, hipStream_t stream)
 {
     g_err.clear();

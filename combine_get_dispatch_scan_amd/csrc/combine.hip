@@ -55,7 +55,9 @@ struct CombineArgs {
     uint16_t* out;
 };
 
-template <int KMAX>
+// UNIT: every weight is 1 (the backward of dispatch); fma(1, v, acc) is the
+// exact sum acc + v, so no weights are read.
+template <int KMAX, bool UNIT>
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineArgs a)
 {
     const int wi = blockIdx.x * kCombineWaves + threadIdx.x / kWave;
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
     float w_own = 0.0f;
     if (lane < a.K) {
         s_own = a.slot[(size_t)t * a.K + lane];
-        w_own = a.w[(size_t)t * a.K + lane];
+        w_own = UNIT ? 1.0f : a.w[(size_t)t * a.K + lane];
     }
     int sk[KMAX];
     float wk[KMAX];
@@ -144,10 +146,16 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slo
     const long long items = (long long)T * a.nseg;
     dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
     dim3 block(kCombineWaves * kWave);
-    if (K <= 2) hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a);
-    else if (K <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a);
-    else if (K <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, stream, a);
+#define EP_COMBINE(KM)                                                                          \
+    do {                                                                                        \
+        if (w) hipLaunchKernelGGL((combine_kernel<KM, false>), grid, block, 0, stream, a);      \
+        else hipLaunchKernelGGL((combine_kernel<KM, true>), grid, block, 0, stream, a);         \
+    } while (0)
+    if (K <= 2) EP_COMBINE(2);
+    else if (K <= 4) EP_COMBINE(4);
+    else if (K <= 8) EP_COMBINE(8);
+    else EP_COMBINE(16);
+#undef EP_COMBINE
     return hipGetLastError();
 }
 

@@ -34,8 +34,14 @@ struct DispatchLaunch {
 
 hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream);
 
+// combine; w == nullptr means unit weights (the backward of dispatch).
 hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
                           const float* w, void* out, hipStream_t stream);
+
+// backward of combine: grad_y rows (and grad_w when y != nullptr).
+hipError_t launch_combine_backward(const void* grad_out, const void* y, int T, int H, int K,
+                                   const int32_t* slot, const float* w, void* grad_y,
+                                   float* grad_w, hipStream_t stream);
 
 hipError_t launch_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 

@@ -186,6 +186,42 @@ int ep_combine(const void* y, const ep_handle_t* handle, const float* topk_weigh
                void* out, hipStream_t stream);
 
 /*
+ * Backward of dispatch: the backward of dispatch is combine (stakiran summary,
+ * section 3 "使うときの流れ"; GeekNews usage section).  With the FP8 cast taken
+ * as straight-through, grad_x[t] = bf16_rne( fp32 sum over dispatched k,
+ * ascending, of grad_recv[slot[t,k]], from +0.0f ); a token with no
+ * dispatched pair gets +0.  Uses the handle of the forward dispatch.
+ *   grad_recv  device bf16 [capacity_rows*H], in the receive order
+ *   grad_x     device bf16 [T*H]
+ * Errors: EP_EINVAL (handle not dispatched, bad pointers), EP_EHIP.
+ */
+int ep_dispatch_backward(const void* grad_recv, const ep_handle_t* handle, void* grad_x,
+                         hipStream_t stream);
+
+/*
+ * Backward of combine: the backward of combine is dispatch (same passages),
+ * of grad_out scaled by each pair's weight, plus the weight gradient:
+ *   grad_y[slot[t,k]] = bf16_rne(w[t,k] * grad_out[t])   (one fp32 product)
+ *   grad_w[t,k]       = <grad_out[t], y[slot[t,k]]>       (fp32; 0 for pairs
+ *                       not dispatched)
+ *   grad_out      device bf16 [T*H]
+ *   y             device bf16 [capacity_rows*H], the forward's expert outputs;
+ *                 NULL when grad_w is NULL
+ *   topk_weights  device fp32 [T*K], or NULL to use the copy dispatch took
+ *   grad_y        device bf16 [capacity_rows*H]; rows no pair maps to are
+ *                 not written
+ *   grad_w        device fp32 [T*K] or NULL.  Each dot product is reduced in
+ *                 a fixed order (per-lane fma chains over the hidden
+ *                 dimension, then a 64-lane tree), so results are
+ *                 deterministic; against the exact sum the error is at most
+ *                 about (H/64 + 6) * 2^-24 * sum_j |grad_out * y|.
+ * Errors: EP_EINVAL, EP_EHIP.
+ */
+int ep_combine_backward(const void* grad_out, const void* y, const ep_handle_t* handle,
+                        const float* topk_weights, void* grad_y, float* grad_w,
+                        hipStream_t stream);
+
+/*
  * Per-expert received counts to the host, for the grouped GEMM (GeekNews
  * usage section: handle.num_recv_tokens_per_expert_list).  Synchronises
  * `stream`.  host_counts: int32 [E] or NULL; host_num_recv: int32 [1] or NULL

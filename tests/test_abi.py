@@ -187,3 +187,25 @@ def test_recv_counts_decode_on_host():
     assert ep.ep_recv_counts_decode(h1, None, None, None) == ep.EP_EINVAL
     assert ep.ep_handle_recv_counts_async(h1, None, None) == ep.EP_EINVAL
     assert ep.ep_handle_recv_counts_async(ep.ep_handle_t(), FAKE, None) == ep.EP_EINVAL
+
+
+def test_backward_calls_validate_before_any_hip_call():
+    h1 = _fake_handle(stage=1)
+    assert ep.ep_dispatch_backward(FAKE, h1, FAKE, None) == ep.EP_EINVAL
+    assert ep.ep_combine_backward(FAKE, FAKE, h1, FAKE, FAKE, FAKE, None) == ep.EP_EINVAL
+    h2 = _fake_handle(stage=2)
+    h2.hidden = 256
+    assert ep.ep_dispatch_backward(FAKE, h2, FAKE + 8, None) == ep.EP_EINVAL
+    assert "grad_x" in ep.ep_last_error()
+    assert ep.ep_dispatch_backward(FAKE + 4, h2, FAKE, None) == ep.EP_EINVAL
+    assert "grad_recv" in ep.ep_last_error()
+    h2.has_weights = 0
+    assert ep.ep_combine_backward(FAKE, FAKE, h2, None, FAKE, FAKE, None) == ep.EP_EINVAL
+    assert "no weights" in ep.ep_last_error()
+    assert ep.ep_combine_backward(FAKE + 8, FAKE, h2, FAKE, FAKE, FAKE, None) == ep.EP_EINVAL
+    assert "grad_out" in ep.ep_last_error()
+    assert ep.ep_combine_backward(FAKE, FAKE, h2, FAKE, None, FAKE, None) == ep.EP_EINVAL
+    assert "grad_y" in ep.ep_last_error()
+    assert ep.ep_combine_backward(FAKE, None, h2, FAKE, FAKE, FAKE, None) == ep.EP_EINVAL
+    assert "needs y" in ep.ep_last_error()
+    assert ep.ep_combine_backward(FAKE, FAKE, h2, FAKE, FAKE, FAKE + 2, None) == ep.EP_EINVAL

@@ -1,0 +1,127 @@
+"""GPU parity of the backward calls against the CPU oracle.
+
+grad_x and grad_y are bit-exact (same fp32 operations); grad_w is an fp32
+dot product reduced in a fixed order on the GPU and in double by the oracle,
+so it is compared within the bound that order implies:
+|gpu - exact| <= (H/64 + 8) * 2^-24 * sum_j |g_j y_j|  (+ the oracle's own
+rounding to fp32), and it must be bit-identical from run to run."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _bf16(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _forward(ep, idx, w, x, E, P, fp8, cap=None):
+    dev = _dev()
+    lay = ep.get_dispatch_layout(torch.from_numpy(idx).to(dev), E, P)
+    recv, sc, h = ep.dispatch(_bf16(x, dev), torch.from_numpy(w).to(dev), lay, fp8, capacity_rows=cap)
+    return h
+
+
+def _check_grad_w(got, ref_exact_f32, g, y, slot, H):
+    gf = workloads.f32_from_bf16_bits(g).astype(np.float64)
+    yf = workloads.f32_from_bf16_bits(y).astype(np.float64)
+    T, K = slot.shape
+    for t in range(T):
+        for k in range(K):
+            s = slot[t, k]
+            if s < 0:
+                assert got[t, k] == 0.0
+                continue
+            mag = np.abs(gf[t] * yf[s]).sum()
+            tol = (H / 64 + 8) * 2.0 ** -24 * mag + 2.0 ** -24 * abs(float(ref_exact_f32[t, k])) + 1e-38
+            assert abs(float(got[t, k]) - float(ref_exact_f32[t, k])) <= tol, (t, k, got[t, k], ref_exact_f32[t, k])
+
+
+CASES = [
+    ("tiny", None),
+    ("skewed", None),
+    ("decode", None),
+    ("v3", None),
+]
+
+
+@pytest.mark.parametrize("name,cap", CASES)
+def test_dispatch_backward_matches_oracle(ep, name, cap):
+    dev = _dev()
+    wl = workloads.config(name)
+    idx, w, x = workloads.make(wl)
+    print(f"[bwd] dispatch_backward {name}", flush=True)
+    ref = oracle.run_all(idx, w, None, wl.E, wl.P, wl.use_fp8)
+    h = _forward(ep, idx, w, x, wl.E, wl.P, wl.use_fp8)
+    g = workloads.random_rows(17, wl.T * wl.K, wl.H, "normal")
+    gx = ep.dispatch_backward(_bf16(g, dev), h)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(gx), oracle.dispatch_backward(g[:ref["rows"]], ref["slot"]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "skewed", "v3"])
+def test_combine_backward_matches_oracle(ep, name):
+    dev = _dev()
+    wl = workloads.config(name)
+    idx, w, x = workloads.make(wl)
+    print(f"[bwd] combine_backward {name}", flush=True)
+    ref = oracle.run_all(idx, w, None, wl.E, wl.P, wl.use_fp8)
+    rows = ref["rows"]
+    h = _forward(ep, idx, w, x, wl.E, wl.P, wl.use_fp8)
+    cap = wl.T * wl.K
+    y = workloads.random_rows(18, cap, wl.H, "normal")
+    g = workloads.random_rows(19, wl.T, wl.H, "normal")
+    t_y, t_g = _bf16(y, dev), _bf16(g, dev)
+    gy_t = torch.full((cap, wl.H), 0x7777, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    gy, gw = ep.combine_backward(t_g, h, y=t_y, grad_y=gy_t)
+    gy2, gw2 = ep.combine_backward(t_g, h, y=t_y)
+    gy3, gw3 = ep.combine_backward(t_g, h)          # grad_y only (segmented launch)
+    torch.cuda.synchronize()
+    ref_gy, ref_gw = oracle.combine_backward(g, y[:rows], ref["slot"], w, cap, fill=0x7777)
+    assert np.array_equal(_bits(gy), ref_gy)
+    assert np.array_equal(_bits(gy2)[:rows], ref_gy[:rows])
+    assert np.array_equal(_bits(gy3)[:rows], ref_gy[:rows])
+    assert gw3 is None
+    got = gw.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), gw2.cpu().numpy().view(np.uint32))   # deterministic
+    sample = slice(0, min(wl.T, 512))
+    _check_grad_w(got[sample], ref_gw[sample], g[sample], y, ref["slot"][sample], wl.H)
+
+
+def test_backward_with_masks_and_capacity(ep):
+    dev = _dev()
+    T, H, E, K, P = 300, 1024, 32, 6, 8
+    idx, w = workloads.random_case(61, T, E, K, mask_frac=0.15, invalid_frac=0.05, dup_frac=0.05,
+                                   distinct=False)
+    x = workloads.random_rows(62, T, H, "normal")
+    N = int(oracle.layout(idx, E, P)["valid"].sum())
+    for cap in (T * K, N - 11):
+        ref = oracle.run_all(idx, w, None, E, P, False, capacity=cap)
+        h = _forward(ep, idx, w, x, E, P, False, cap=cap)
+        y = workloads.random_rows(63, cap, H, "wide")
+        g = workloads.random_rows(64, T, H, "wide")
+        gr = workloads.random_rows(65, cap, H, "normal")
+        gx = ep.dispatch_backward(_bf16(gr, dev), h)
+        gy, gw = ep.combine_backward(_bf16(g, dev), h, y=_bf16(y, dev))
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(gx), oracle.dispatch_backward(gr, ref["slot"]))
+        ref_gy, ref_gw = oracle.combine_backward(g, y, ref["slot"], w, cap)
+        used = np.zeros(cap, bool)
+        used[ref["slot"][ref["slot"] >= 0]] = True
+        assert np.array_equal(_bits(gy)[used], ref_gy[used])
+        _check_grad_w(gw.cpu().numpy(), ref_gw, g, y, ref["slot"], H)
