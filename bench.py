@@ -240,6 +240,40 @@ def main():
         a1.record(stream)
         torch.cuda.synchronize()
         return nbytes * reps / (a0.elapsed_time(a1) * 1e-3) / 1e9
+    # backward calls on the same routing (reported beside the forward step):
+    # dispatch backward = unit-weight combine of a [rows, H] gradient;
+    # combine backward = weight-scaled rows of grad_out plus grad_w dot products
+    grad_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    grad_y = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    grad_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+
+    def time_call(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        evs_b = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in evs_b:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return mean([e[0].elapsed_time(e[1]) for e in evs_b])
+
+    def _ok(rc):
+        if rc != 0:
+            raise RuntimeError(ep.ep_last_error())
+    db_ms = time_call(lambda: _ok(ep.ep_dispatch_backward(p(t_y), h, p(grad_x), sp)))
+    cb_ms = time_call(lambda: _ok(ep.ep_combine_backward(p(out), p(t_y), h, None, p(grad_y),
+                                                         p(grad_w), sp)))
+    db_bytes = N * H * 2 + T * H * 2 + T * K * 4
+    cb_bytes = T * H * 2 + 2 * N * H * 2 + T * K * 12
+    backward = {
+        "dispatch_backward_us": round(db_ms * 1e3, 2),
+        "dispatch_backward_hbm_frac": round(db_bytes / (db_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "combine_backward_us": round(cb_ms * 1e3, 2),
+        "combine_backward_hbm_frac": round(cb_bytes / (cb_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+    del grad_x, grad_y, grad_w
+
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     copy_gbps = rate(lambda: dst.copy_(src), 2 << 30)
@@ -274,6 +308,7 @@ def main():
         },
         "phases_us": {k: round(v * 1e3, 2) for k, v in phases.items()},
         "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},
+        "backward": backward,
         "logical_GBps": {
             "dispatch": round(bc["dispatch_logical"] / ((phases["layout"] + phases["dispatch"]) * 1e-3) / 1e9, 1),
             "combine": round(bc["combine_logical"] / (phases["combine"] * 1e-3) / 1e9, 1),

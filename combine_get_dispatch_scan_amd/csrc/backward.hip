@@ -8,10 +8,12 @@
 // The first is a weight-scaled BF16 dispatch of grad_out along the forward
 // routing; the second needs the forward's expert outputs y.
 //
-// Work item = one wave.  Without grad_w the row is split into segments like
-// dispatch.  With grad_w a wave owns the whole row, so each dot product is
-// reduced in a fixed order: a per-lane fma chain over the lane's channels,
-// then an xor-shuffle tree over the 64 lanes (deterministic).
+// Without grad_w a work item is one wave on a segment of the row, as in
+// dispatch.  With grad_w a workgroup of 4 waves owns one token: wave w takes
+// the wave steps w, w+4, w+8, ... of the row, and each dot product is reduced
+// in a fixed order -- a per-lane fma chain over the lane's channels, an
+// xor-shuffle tree over the 64 lanes, then the 4 waves' partial sums added in
+// wave order through LDS -- so grad_w is deterministic.
 #include "device.h"
 #include "launch.h"
 
@@ -32,6 +34,11 @@ struct CombineBwdArgs {
     float* grad_w;
 };
 
+__device__ __forceinline__ int slot_of(const CombineBwdArgs& a, int t, int k)
+{
+    return a.slot[(size_t)t * a.K + k];
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll
@@ -43,9 +50,12 @@ __device__ __forceinline__ float wave_sum(float v)
 template <int KMAX, bool WGRAD>
 __global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(CombineBwdArgs a)
 {
-    const int wi = blockIdx.x * kBwdWaves + threadIdx.x / kWave;
-    const int t = wi / a.nseg;
-    const int seg = wi % a.nseg;
+    __shared__ float lds_part[kBwdWaves][16];
+    const int wave = threadIdx.x / kWave;
+    const int wi = blockIdx.x * kBwdWaves + wave;
+    // WGRAD: token = block, the block's waves interleave over the row's steps
+    const int t = WGRAD ? (int)blockIdx.x : wi / a.nseg;
+    const int seg = WGRAD ? 0 : wi % a.nseg;
     if (t >= a.T)
         return;
     const int lane = lane_id();
@@ -69,16 +79,18 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(Com
 
     const int H = a.H;
     const uint16_t* grow = a.grad_out + (size_t)t * H;
-    const int i_begin = seg * a.iters_per_seg;
-    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
+    // steps i_begin, i_begin + stride, ... below i_end
+    const int stride = WGRAD ? kBwdWaves : 1;
+    const int i_begin = WGRAD ? wave : seg * a.iters_per_seg;
+    const int i_end = WGRAD ? a.iters : min(a.iters, i_begin + a.iters_per_seg);
 
-    for (int i0 = i_begin; i0 < i_end; i0 += kBwdUnroll) {
+    for (int i0 = i_begin; i0 < i_end; i0 += kBwdUnroll * stride) {
         u32x4 g[kBwdUnroll];
         u32x4 yv[kBwdUnroll][KMAX];
 #pragma unroll
         for (int u = 0; u < kBwdUnroll; ++u) {
-            const int cb = (i0 + u) * kBwdChPerIter + lane * 8;
-            const bool active = (i0 + u < i_end) && cb < H;
+            const int cb = (i0 + u * stride) * kBwdChPerIter + lane * 8;
+            const bool active = (i0 + u * stride < i_end) && cb < H;
             if (active)
                 g[u] = load16_hint<true>(grow + cb);
             if (WGRAD) {
@@ -90,8 +102,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(Com
         }
 #pragma unroll
         for (int u = 0; u < kBwdUnroll; ++u) {
-            const int cb = (i0 + u) * kBwdChPerIter + lane * 8;
-            const bool active = (i0 + u < i_end) && cb < H;
+            const int cb = (i0 + u * stride) * kBwdChPerIter + lane * 8;
+            const bool active = (i0 + u * stride < i_end) && cb < H;
             if (!active)
                 continue;
             float gf[8];
@@ -122,11 +134,18 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(Com
     if (WGRAD) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (k >= a.K)
-                break;
             const float s = wave_sum(dot[k]);
             if (lane == 0)
-                a.grad_w[(size_t)t * a.K + k] = sk[k] >= 0 ? s : 0.0f;
+                lds_part[wave][k] = s;
+        }
+        __syncthreads();
+        if (threadIdx.x < a.K) {
+            const int k = threadIdx.x;
+            float s = lds_part[0][k];
+#pragma unroll
+            for (int v = 1; v < kBwdWaves; ++v)
+                s += lds_part[v][k];
+            a.grad_w[(size_t)t * a.K + k] = slot_of(a, t, k) >= 0 ? s : 0.0f;
         }
     }
 }
@@ -149,17 +168,19 @@ hipError_t launch_combine_backward(const void* grad_out, const void* y, int T, i
     a.grad_w = grad_w;
     a.iters = (H + kBwdChPerIter - 1) / kBwdChPerIter;
     const bool wgrad = grad_w != nullptr;
+    dim3 grid;
     if (wgrad) {
-        // a whole row per wave keeps each dot product's reduction order fixed
+        // one workgroup per token keeps each dot product's reduction order fixed
         a.nseg = 1;
         a.iters_per_seg = a.iters;
+        grid = dim3((unsigned)T);
     } else {
         const RowSplit rs = split_rows(T, a.iters, 65536, 4);
         a.nseg = rs.nseg;
         a.iters_per_seg = rs.iters_per_seg;
+        const long long items = (long long)T * a.nseg;
+        grid = dim3((unsigned)((items + kBwdWaves - 1) / kBwdWaves));
     }
-    const long long items = (long long)T * a.nseg;
-    dim3 grid((unsigned)((items + kBwdWaves - 1) / kBwdWaves));
     dim3 block(kBwdWaves * kWave);
 #define EP_BWD(KM)                                                                                   \
     do {                                                                                             \
