@@ -60,6 +60,8 @@ def lib():
         L.oracle_expert_offsets.restype = None
         L.oracle_slots.argtypes = [P, P, i32, i32, P, i32, i32, P, P, P]
         L.oracle_slots.restype = None
+        L.oracle_slots_static.argtypes = [P, P, i32, i32, i32, i32, P, P]
+        L.oracle_slots_static.restype = None
         L.oracle_dispatch.argtypes = [P, i32, i32, i32, P, i32, P, P]
         L.oracle_dispatch.restype = None
         L.oracle_combine.argtypes = [P, i32, i32, i32, P, P, P]
@@ -148,6 +150,29 @@ def slots(topk_idx: np.ndarray, valid: np.ndarray, off: np.ndarray, capacity: in
     ovf = np.zeros(1, np.int32)
     lib().oracle_slots(_p(idx), _p(valid), T, K, _p(off), E, capacity, _p(slot), _p(src), _p(ovf))
     return slot, src[:capacity], int(ovf[0])
+
+
+def slots_static(topk_idx: np.ndarray, valid: np.ndarray, E: int, cap: int):
+    """Low-latency layout: returns (slot [T,K] int32, overflow int)."""
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    valid = _c(valid, np.uint8)
+    slot = np.empty((T, K), np.int32)
+    ovf = np.zeros(1, np.int32)
+    lib().oracle_slots_static(_p(idx), _p(valid), T, K, E, cap, _p(slot), _p(ovf))
+    return slot, int(ovf[0])
+
+
+def run_low_latency(topk_idx, topk_weights, x_bits, E, P, use_fp8, cap):
+    """The low-latency path on the CPU: layout counts, static-capacity slots
+    and the permute into E*cap rows (unused rows stay zero)."""
+    lay = layout(topk_idx, E, P)
+    slot, ovf = slots_static(topk_idx, lay["valid"], E, cap)
+    res = dict(lay, slot=slot, overflow=ovf, rows=E * cap)
+    if x_bits is not None:
+        recv, scales = dispatch(x_bits, slot, E * cap, use_fp8)
+        res.update(recv_x=recv, recv_scales=scales)
+    return res
 
 
 def dispatch(x_bits: np.ndarray, slot: np.ndarray, rows: int, use_fp8: bool):

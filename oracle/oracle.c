@@ -223,6 +223,33 @@ void oracle_slots(const int64_t* topk_idx, const uint8_t* valid, int T, int K,
     free(cur);
 }
 
+/* Low-latency layout: each expert has a fixed block of cap rows, filled in
+ * ascending token order. */
+void oracle_slots_static(const int64_t* topk_idx, const uint8_t* valid, int T, int K, int E,
+                         int cap, int32_t* slot, int32_t* overflow)
+{
+    int32_t* cur = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+    *overflow = 0;
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            size_t i = (size_t)t * K + k;
+            if (!valid[i]) {
+                slot[i] = -1;
+                continue;
+            }
+            int e = (int)topk_idx[i];
+            int32_t r = cur[e]++;
+            if (r < cap) {
+                slot[i] = (int32_t)e * cap + r;
+            } else {
+                slot[i] = -1;
+                *overflow = 1;
+            }
+        }
+    }
+    free(cur);
+}
+
 /* dispatch routes each token row to every expert it selected; BF16 and FP8
  * payloads are both supported (GeekNews usage section: "supports BF16 and FP8
  * input"; FP8 dispatch / BF16 combine in the V3 benchmark setup).  In FP8 mode

@@ -63,6 +63,14 @@ void oracle_slots(const int64_t* topk_idx, const uint8_t* valid, int T, int K,
                   const int32_t* off, int E, int capacity,
                   int32_t* slot, int32_t* src_token, int32_t* overflow);
 
+/* Static-capacity receive layout of the low-latency dispatch (devtrends.ru,
+ * "Как это выглядит в коде": low_latency_dispatch(hidden_states, topk_idx,
+ * num_max_tokens, num_experts)): expert e owns rows [e*cap, (e+1)*cap), and a
+ * dispatched pair takes row e*cap + (number of earlier tokens that chose e).
+ * A pair whose rank reaches cap is dropped (slot -1) and *overflow = 1. */
+void oracle_slots_static(const int64_t* topk_idx, const uint8_t* valid, int T, int K, int E,
+                         int cap, int32_t* slot, int32_t* overflow);
+
 /* Step 3, permute (BF16: bit copy of the row) or quantise-then-permute (FP8).
  * recv has capacity rows of H elements (uint16 bf16 or uint8 e4m3fn);
  * scales has capacity rows of H/128 fp32 (FP8 mode only). */

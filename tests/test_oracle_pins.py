@@ -565,3 +565,35 @@ def test_combine_backward_grad_y_single_rounding():
             s = r["slot"][t, k]
             ref = (gt[t] * torch.tensor(float(w[t, k]), dtype=torch.float32)).to(torch.bfloat16)
             assert np.array_equal(gy[s], ref.view(torch.int16).numpy().view(np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# low-latency (static-capacity) layout
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,K,cap", [(128, 256, 8, 16), (200, 16, 4, 64), (64, 8, 3, 5), (1, 4, 2, 1)])
+@pytest.mark.parametrize("mode", ["clean", "dirty"])
+def test_static_slots_against_stable_sort(T, E, K, cap, mode):
+    """slot = e*cap + rank, rank = position of the pair among expert e's pairs
+    in a textbook stable sort by expert id; pairs ranked >= cap are dropped."""
+    kw = {} if mode == "clean" else dict(distinct=False, mask_frac=0.1, invalid_frac=0.05, dup_frac=0.1)
+    idx, _ = workloads.random_case(T + cap, T, E, K, **kw)
+    valid = _valid_independent(idx, E)
+    slot, ovf = oracle.slots_static(idx, valid, E, cap)
+    key = np.where(valid.reshape(-1) == 1, idx.reshape(-1), np.int64(1) << 62)
+    order = np.argsort(key, kind="stable")
+    pos = np.empty(order.size, np.int64)
+    pos[order] = np.arange(order.size)
+    cnt = np.bincount(idx[valid == 1], minlength=E)
+    first = np.concatenate([[0], np.cumsum(cnt)])[:E]
+    flat_idx = idx.reshape(-1)
+    exp = np.full(T * K, -1, np.int64)
+    ok = valid.reshape(-1) == 1
+    rank = pos[ok] - first[flat_idx[ok]]
+    exp[np.nonzero(ok)[0]] = np.where(rank < cap, flat_idx[ok] * cap + rank, -1)
+    assert np.array_equal(slot.reshape(-1), exp)
+    assert ovf == int((cnt > cap).any())
+    # rows are distinct and inside the owning expert's block
+    s = slot[slot >= 0]
+    assert np.unique(s).size == s.size
+    assert np.all(s // cap == idx[slot >= 0])
