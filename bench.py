@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--config", default="v3", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--low-latency", action="store_true",
+                    help="one-launch static-capacity dispatch (T <= 256) instead of layout + dispatch")
+    ap.add_argument("--ll-cap", type=int, default=0,
+                    help="rows per expert for --low-latency (default: T, so nothing is dropped)")
     return ap.parse_args()
 
 
@@ -72,7 +76,11 @@ KERNEL_SOURCES = {
     "combine_kernel": ["combine_get_dispatch_scan_amd/csrc/combine.hip",
                        "combine_get_dispatch_scan_amd/csrc/device.h"],
     "dispatch_fp8_kernel": ["combine_get_dispatch_scan_amd/csrc/dispatch.hip",
+                            "combine_get_dispatch_scan_amd/csrc/dispatch_rows.h",
                             "combine_get_dispatch_scan_amd/csrc/device.h"],
+    "low_latency_dispatch_kernel": ["combine_get_dispatch_scan_amd/csrc/low_latency.hip",
+                                    "combine_get_dispatch_scan_amd/csrc/dispatch_rows.h",
+                                    "combine_get_dispatch_scan_amd/csrc/device.h"],
 }
 
 
@@ -110,6 +118,150 @@ def cpu_baseline(wl, idx, w, x, y, runs):
     return statistics.median(times), r["N"]
 
 
+def bench_low_latency(args):
+    """Decode step through the one-launch dispatch: ep_low_latency_dispatch ->
+    counts readback -> ep_combine, timed eagerly and as a replayed HIP graph
+    (dispatch + combine captured once)."""
+    import torch
+    import combine_get_dispatch_scan_amd as ep
+    import workloads
+
+    ep.load()
+    dev = torch.device("cuda:0")
+    wl = workloads.config(args.config)
+    T, H, K, E, P = wl.T, wl.H, wl.K, wl.E, wl.P
+    if T > 256:
+        print(f"--low-latency takes at most 256 tokens ({args.config} has {T})", file=sys.stderr)
+        sys.exit(2)
+    cap = args.ll_cap or T
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    y = workloads.expert_outputs(wl, E * cap)
+    t_idx = torch.from_numpy(idx).to(dev)
+    t_w = torch.from_numpy(w).to(dev)
+    t_x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    t_y = torch.from_numpy(y.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    host_buf = torch.empty(E + 5, dtype=torch.int32, pin_memory=True)
+    counts = (ctypes.c_int32 * E)()
+    nrecv = ctypes.c_int32(0)
+    counts_ready = torch.cuda.Event()
+    recv, sc, lay = ep.low_latency_dispatch(t_x, t_idx, t_w, E, P, cap, wl.use_fp8)
+    h = lay.handle.c
+    ws = lay.handle.ws
+    stream = torch.cuda.current_stream()
+    sp = ep._stream()
+    p = lambda t: None if t is None else t.data_ptr()
+    mean = lambda v: sum(v) / len(v)
+    ll_args = (p(t_x), p(t_idx), p(t_w), T, H, K, E, P, int(wl.use_fp8), cap, p(recv), p(sc),
+               p(lay.num_tokens_per_partition), p(lay.num_tokens_per_expert),
+               p(lay.is_token_in_partition), p(lay.num_invalid), p(ws), ws.numel(), h, sp)
+
+    def fwd():
+        s_now = ep._stream()          # the capture stream under graph capture
+        rc = ep.ep_low_latency_dispatch(*ll_args[:-1], s_now)
+        rc |= ep.ep_combine(p(t_y), h, None, p(out), s_now)
+        if rc != 0:
+            raise RuntimeError(ep.ep_last_error())
+
+    def step():
+        rc = ep.ep_low_latency_dispatch(*ll_args)
+        rc |= ep.ep_handle_recv_counts_async(h, host_buf.data_ptr(), sp)
+        counts_ready.record(stream)
+        rc |= ep.ep_combine(p(t_y), h, None, p(out), sp)
+        # the grouped GEMM would need the counts here; combine is already queued
+        counts_ready.synchronize()
+        rc |= ep.ep_recv_counts_decode(h, host_buf.data_ptr(), counts, ctypes.byref(nrecv))
+        if rc != 0:
+            raise RuntimeError(ep.ep_last_error())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert nrecv.value == N, (nrecv.value, N)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # kernel duration: back-to-back launches keep the GPU busy, so events
+    # around a batch time the kernels rather than the host's launch gaps
+    def batch_us(fn, n=200):
+        fn()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(n):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / n
+    disp_us = batch_us(lambda: ep.ep_low_latency_dispatch(*ll_args))
+    comb_us = batch_us(lambda: ep.ep_combine(p(t_y), h, None, p(out), sp))
+    disp_ms = disp_us * 1e-3
+    # a plain 1 GiB copy and fill in the same run (the counters' calibration)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    copy_gbps = (2 << 30) / (batch_us(lambda: dst.copy_(src), 5) * 1e-6) / 1e9
+    fill_gbps = (1 << 30) / (batch_us(lambda: dst.fill_(3), 5) * 1e-6) / 1e9
+    del src, dst
+
+    # the same forward captured once and replayed (no host work per step)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fwd()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(f"[bench] low-latency {args.config}: {ms_per_step * 1e3:.1f} us/step eager, "
+          f"{graph_ms * 1e3:.1f} us/step graph, kernels: dispatch {disp_us:.2f} us, "
+          f"combine {comb_us:.2f} us",
+          file=sys.stderr, flush=True)
+
+    b = 1 if wl.use_fp8 else 2
+    nb = H // 128
+    disp_logical = N * (H * b + (4 * nb if wl.use_fp8 else 0))
+    comb_logical = N * H * 2
+    # ids and weights read, slots + weight copy + mask + counts written, x read once, rows written
+    disp_alg = (T * K * 8 + T * K * 4 + T * K * 8 + T * P + (2 * E + P + 8) * 4 + T * H * 2
+                + disp_logical)
+    disp_gbps = disp_alg / (disp_ms * 1e-3) / 1e9
+    value = (disp_logical + comb_logical) / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": "low-latency dispatch & combine logical GB/s on 1 MI355X",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16/fp32-acc" if wl.use_fp8 else "bf16/fp32-acc", "data": "synthetic",
+        "config": {"workload": DESCR[args.config] + ", one-launch static-capacity dispatch",
+                   "tokens": T, "hidden": H, "experts": E, "topk": K, "partitions": P,
+                   "dispatched_pairs": N, "rows_per_expert": cap},
+        "graph_replay_us_per_step": round(graph_ms * 1e3, 2),
+        "kernels_us": {"low_latency_dispatch": round(disp_us, 2), "combine": round(comb_us, 2)},
+        "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},
+        "roofline": {"bound": "hbm", "kernel": "low_latency_dispatch_kernel",
+                     "achieved": round(disp_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(disp_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": disp_alg,
+                     "avg_launch_us": round(disp_ms * 1e3, 2),
+                     "traffic": measured_traffic(f"{args.config}_low_latency", "low_latency_dispatch_kernel")},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -117,6 +269,8 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the path runs on one MI355X and is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
+    if args.low_latency:
+        return bench_low_latency(args)
 
     import torch
     import combine_get_dispatch_scan_amd as ep

@@ -53,7 +53,7 @@ class ep_handle_t(ctypes.Structure):
         ("capacity_rows", ctypes.c_int32),
         ("has_weights", ctypes.c_int32),
         ("num_chunks", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("static_cap", ctypes.c_int32),
         ("ws", ctypes.c_void_p),
         ("ws_bytes", ctypes.c_size_t),
         ("expert_offset", ctypes.c_void_p),
@@ -82,6 +82,8 @@ _SIGS = {
                                 ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_dispatch": ([_P, _P, _I, _I, _P, _P, _I, ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_dispatch_cached": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_low_latency_dispatch": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                                 _P, ctypes.c_size_t, ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_combine": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_dispatch_backward": ([_P, ctypes.POINTER(ep_handle_t), _P, _P], _I),
     "ep_combine_backward": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P, _P, _P], _I),
@@ -142,6 +144,19 @@ def ep_dispatch(x, topk_weights, hidden, use_fp8, recv_x, recv_scales, capacity_
                 stream) -> int:
     return load().ep_dispatch(x, topk_weights, hidden, int(use_fp8), recv_x, recv_scales,
                               capacity_rows, ctypes.byref(handle), stream)
+
+
+def ep_low_latency_dispatch(x, topk_idx, topk_weights, num_tokens, hidden, num_topk, num_experts,
+                            num_partitions, use_fp8, num_max_tokens, recv_x, recv_scales,
+                            num_tokens_per_partition, num_tokens_per_expert,
+                            is_token_in_partition, num_invalid, ws, ws_bytes, handle,
+                            stream) -> int:
+    return load().ep_low_latency_dispatch(x, topk_idx, topk_weights, num_tokens, hidden, num_topk,
+                                          num_experts, num_partitions, int(use_fp8),
+                                          num_max_tokens, recv_x, recv_scales,
+                                          num_tokens_per_partition, num_tokens_per_expert,
+                                          is_token_in_partition, num_invalid, ws, ws_bytes,
+                                          ctypes.byref(handle), stream)
 
 
 def ep_dispatch_cached(x, handle, recv_x, recv_scales, stream) -> int:
@@ -211,9 +226,10 @@ class Handle:
 
     def _view(self, field, n, dtype):
         import torch
-        if n == 0:
+        ptr = getattr(self.c, field)
+        if n == 0 or not ptr:
             return torch.empty(0, dtype=dtype, device=self.ws.device)
-        off = getattr(self.c, field) - self.ws.data_ptr()
+        off = ptr - self.ws.data_ptr()
         return self.ws[off:off + n * 4].view(dtype)
 
     @property
@@ -289,6 +305,44 @@ def dispatch(x, topk_weights, layout: Layout, use_fp8: bool, capacity_rows: Opti
     _check(ep_dispatch(_ptr(x), _ptr(topk_weights), H, int(use_fp8), _ptr(recv), _ptr(scales),
                        cap, h.c, _stream()))
     return recv, scales, h
+
+
+def low_latency_dispatch(x, topk_idx, topk_weights, num_experts: int, num_partitions: int,
+                         num_max_tokens: int, use_fp8: bool, ws=None, out=None):
+    """One-launch dispatch for decode batches (T <= 256) into a static
+    per-expert layout: expert e's rows are [e*cap, (e+1)*cap).  Returns
+    (recv_x [E*cap, H], recv_scales or None, Layout).  ``out`` may pass
+    preallocated (recv_x, recv_scales, Layout) to reuse (e.g. under graph
+    capture)."""
+    import torch
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    topk_idx = topk_idx.contiguous()
+    E, P, cap = num_experts, num_partitions, num_max_tokens
+    dev = x.device
+    if out is None:
+        if ws is None:
+            ws = torch.empty(ep_workspace_bytes(T, K, E, P), dtype=torch.uint8, device=dev)
+        lay = Layout(torch.empty(P, dtype=torch.int32, device=dev),
+                     torch.empty(E, dtype=torch.int32, device=dev),
+                     torch.empty((T, P), dtype=torch.uint8, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev), Handle(ep_handle_t(), ws))
+        if use_fp8:
+            recv = torch.empty((E * cap, H), dtype=torch.float8_e4m3fn, device=dev)
+            scales = torch.empty((E * cap, H // 128), dtype=torch.float32, device=dev)
+        else:
+            recv = torch.empty((E * cap, H), dtype=torch.bfloat16, device=dev)
+            scales = None
+    else:
+        recv, scales, lay = out
+    h = lay.handle
+    _check(ep_low_latency_dispatch(_ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, K, E, P,
+                                   int(use_fp8), cap, _ptr(recv), _ptr(scales),
+                                   _ptr(lay.num_tokens_per_partition),
+                                   _ptr(lay.num_tokens_per_expert),
+                                   _ptr(lay.is_token_in_partition), _ptr(lay.num_invalid),
+                                   _ptr(h.ws), h.ws.numel(), h.c, _stream()))
+    return recv, scales, lay
 
 
 def dispatch_cached(x, handle: Handle, recv_x=None, recv_scales=None):

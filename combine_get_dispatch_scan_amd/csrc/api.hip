@@ -175,9 +175,11 @@ static int check_rows(const ep_handle_t* h, const void* x, int H, int use_fp8, c
         return fail(EP_EINVAL, "use_fp8 must be 0 or 1");
     if (use_fp8 && H % 128 != 0)
         return fail(EP_EINVAL, "FP8 dispatch needs hidden %% 128 == 0 (hidden=%d)", H);
-    if (capacity < 0 || (int64_t)capacity > (int64_t)T * h->num_topk)
-        return fail(EP_EINVAL, "capacity_rows=%d must be in [0, T*K=%lld]", capacity,
-                    (long long)T * h->num_topk);
+    const int64_t max_rows = h->static_cap ? (int64_t)h->num_experts * h->static_cap
+                                           : (int64_t)T * h->num_topk;
+    if (capacity < 0 || (int64_t)capacity > max_rows)
+        return fail(EP_EINVAL, "capacity_rows=%d must be in [0, %lld]", capacity,
+                    (long long)max_rows);
     if (T > 0 && (!x || !aligned(x, 16)))
         return fail(EP_EINVAL, "x must be a non-NULL 16-byte aligned device pointer");
     if (capacity > 0 && (!recv_x || !aligned(recv_x, 16)))
@@ -223,6 +225,8 @@ int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp
     int rc = check_handle(handle, 1);
     if (rc)
         return rc;
+    if (handle->static_cap)
+        return fail(EP_EINVAL, "handle holds a low-latency (static) layout: use ep_dispatch_cached");
     rc = check_rows(handle, x, hidden, use_fp8, recv_x, recv_scales, capacity_rows);
     if (rc)
         return rc;
@@ -237,6 +241,99 @@ int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp
     if (rc)
         return rc;
     h.stage = 2;
+    *handle = h;
+    return EP_OK;
+}
+
+int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                            int T, int H, int K, int E, int P, int use_fp8, int cap,
+                            void* recv_x, float* recv_scales,
+                            int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_partition, int32_t* num_invalid,
+                            void* ws, size_t ws_bytes, ep_handle_t* handle, hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_dims(T, K, E, P);
+    if (rc)
+        return rc;
+    if (!handle)
+        return fail(EP_EINVAL, "handle is NULL");
+    if (T > EP_MAX_LL_TOKENS)
+        return fail(EP_EINVAL, "low-latency dispatch takes at most %d tokens (got %d)",
+                    EP_MAX_LL_TOKENS, T);
+    if (cap < 1 || (int64_t)E * cap >= (int64_t)1 << 31)
+        return fail(EP_EINVAL, "num_max_tokens=%d must be >= 1 with E*num_max_tokens < 2^31", cap);
+    if (T > 0 && (!topk_idx || !aligned(topk_idx, 8)))
+        return fail(EP_EINVAL, "topk_idx must be a non-NULL 8-byte aligned device pointer");
+    if (T > 0 && !is_token_in_partition)
+        return fail(EP_EINVAL, "is_token_in_partition is NULL");
+    if (!num_tokens_per_partition || !num_tokens_per_expert || !num_invalid ||
+        !aligned(num_tokens_per_partition, 4) || !aligned(num_tokens_per_expert, 4) ||
+        !aligned(num_invalid, 4))
+        return fail(EP_EINVAL, "count outputs must be non-NULL 4-byte aligned device pointers");
+    if (topk_weights && !aligned(topk_weights, 4))
+        return fail(EP_EINVAL, "topk_weights must be 4-byte aligned");
+    const WsLayout L = ws_layout(T, K, E, P);
+    if (!ws || !aligned(ws, kAlign))
+        return fail(EP_EINVAL, "workspace must be a non-NULL 256-byte aligned device pointer");
+    if (ws_bytes < L.total)
+        return fail(EP_EINVAL, "workspace too small: %zu bytes given, %zu needed", ws_bytes, L.total);
+
+    char* w = static_cast<char*>(ws);
+    ep_handle_t h;
+    memset(&h, 0, sizeof h);
+    h.magic = EP_HANDLE_MAGIC;
+    h.stage = 1;
+    h.num_tokens = T;
+    h.num_topk = K;
+    h.num_experts = E;
+    h.num_partitions = P;
+    h.num_chunks = (T + kChunk - 1) / kChunk;
+    h.ws = ws;
+    h.ws_bytes = ws_bytes;
+    h.expert_offset = reinterpret_cast<int32_t*>(w + L.expert_offset);
+    h.slot = reinterpret_cast<int32_t*>(w + L.slot);
+    h.src_token = nullptr;      // static layout: rows are found from slot alone
+    h.static_cap = cap;
+    h.weights = reinterpret_cast<float*>(w + L.weights);
+    h.status = reinterpret_cast<int32_t*>(w + L.status);
+    rc = check_rows(&h, x, H, use_fp8, recv_x, recv_scales, 0);
+    if (rc)
+        return rc;
+    if (T > 0 && (!recv_x || !aligned(recv_x, 16)))
+        return fail(EP_EINVAL, "recv_x must be a non-NULL 16-byte aligned device pointer");
+    if (T > 0 && use_fp8 && (!recv_scales || !aligned(recv_scales, 4)))
+        return fail(EP_EINVAL, "recv_scales must be a non-NULL 4-byte aligned device pointer");
+
+    moe_ep::LowLatencyLaunch LL;
+    LL.x = x;
+    LL.topk_idx = topk_idx;
+    LL.w_in = topk_weights;
+    LL.T = T;
+    LL.H = H;
+    LL.K = K;
+    LL.E = E;
+    LL.P = P;
+    LL.cap = cap;
+    LL.use_fp8 = use_fp8;
+    LL.recv = recv_x;
+    LL.scales = recv_scales;
+    LL.slot = h.slot;
+    LL.w_copy = h.weights;
+    LL.status = h.status;
+    LL.expert_offset = h.expert_offset;
+    LL.num_tokens_per_expert = num_tokens_per_expert;
+    LL.num_tokens_per_partition = num_tokens_per_partition;
+    LL.is_token_in_partition = is_token_in_partition;
+    LL.num_invalid = num_invalid;
+    hipError_t e = moe_ep::launch_low_latency_dispatch(LL, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "low-latency dispatch launch");
+    h.stage = 2;
+    h.hidden = H;
+    h.use_fp8 = use_fp8;
+    h.capacity_rows = E * cap;
+    h.has_weights = topk_weights != nullptr;
     *handle = h;
     return EP_OK;
 }
@@ -364,7 +461,7 @@ int ep_recv_counts_decode(const ep_handle_t* handle, const int32_t* host_buf,
     if (host_num_recv)
         *host_num_recv = off[E];
     if (handle->stage >= 2 && st[0])
-        return fail(EP_ECAPACITY, "dispatch dropped pairs: N=%d > capacity_rows=%d", off[E],
+        return fail(EP_ECAPACITY, "dispatch dropped pairs: they did not fit capacity_rows=%d",
                     handle->capacity_rows);
     if (st[1] > 0)
         return fail(EP_EIDS, "topk_idx held %d out-of-range or repeated ids", st[1]);

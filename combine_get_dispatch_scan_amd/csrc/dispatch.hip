@@ -8,48 +8,13 @@
 // Work item = (token, segment of the row), one wave each.  Lanes 0..K-1 turn
 // the pair codes left by the layout step into receive rows
 //     slot = expert_offset[e] + chunk_base[chunk][e] + rank_in_chunk
-// and broadcast them to the wave (readlane -> SGPRs).  The row is then read
-// once with 16-byte loads and written K times with 16-byte stores.  In FP8
-// mode each lane holds 16 consecutive channels, so 8 lanes cover one
-// 128-channel block: amax is reduced over those 8 lanes, the block's inverse
-// scale 448/a is one correctly rounded fp32 division, and every value is
-// multiplied by it and encoded to E4M3FN before the K stores.
+// and broadcast them to the wave (readlane -> SGPRs); the row itself is then
+// handled by fp8_rows / bf16_rows (dispatch_rows.h).
 #include "device.h"
+#include "dispatch_rows.h"
 #include "launch.h"
 
 namespace moe_ep {
-
-#ifndef EP_DISPATCH_UNROLL
-#define EP_DISPATCH_UNROLL 2
-#endif
-#ifndef EP_DISPATCH_MIN_ITEMS
-#define EP_DISPATCH_MIN_ITEMS 65536
-#endif
-#ifndef EP_DISPATCH_MAX_ITERS
-#define EP_DISPATCH_MAX_ITERS 4
-#endif
-#ifndef EP_DISPATCH_WAVES
-#define EP_DISPATCH_WAVES 4
-#endif
-// Issue the first row loads before the slot prologue (measured 2-3 us slower
-// at the V3 shape, so off).
-#ifndef EP_DISPATCH_LOAD_FIRST
-#define EP_DISPATCH_LOAD_FIRST 0
-#endif
-// Cache hints of the row traffic.  Measured on MI355X at the V3 shape: plain
-// loads of x with non-temporal stores of the received rows is fastest (~98 us
-// against ~125 us with both non-temporal and ~138 us with plain stores).
-#ifndef EP_DISPATCH_NT_LOAD
-#define EP_DISPATCH_NT_LOAD 0
-#endif
-#ifndef EP_DISPATCH_NT_STORE
-#define EP_DISPATCH_NT_STORE 1
-#endif
-
-constexpr int kDispatchWaves = EP_DISPATCH_WAVES;   // waves per workgroup
-constexpr int kFp8ChPerIter = kWave * 16;           // 1024 channels per wave step
-constexpr int kBf16ChPerIter = kWave * 8;           // 512 channels per wave step
-constexpr int kDispatchUnroll = EP_DISPATCH_UNROLL; // wave steps with loads in flight
 
 struct DispatchArgs {
     const uint16_t* x;
@@ -110,86 +75,15 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(Di
     const int seg = wi % a.nseg;
     if (t >= a.T)
         return;
-    const int lane = lane_id();
-    const int H = a.H;
-    const int nb = H / kQBlock;
-    const uint16_t* xrow = a.x + (size_t)t * H;
-    uint8_t* recv = static_cast<uint8_t*>(a.recv);
-    const int i_begin = seg * a.iters_per_seg;
-    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
-
-    u32x4 lo[kDispatchUnroll], hi[kDispatchUnroll];
-    auto load_steps = [&](int i0) {
-#pragma unroll
-        for (int u = 0; u < kDispatchUnroll; ++u) {
-            const int cb = (i0 + u) * kFp8ChPerIter + lane * 16;
-            if (i0 + u < i_end && cb < H) {
-                lo[u] = load16_hint<EP_DISPATCH_NT_LOAD>(xrow + cb);
-                hi[u] = load16_hint<EP_DISPATCH_NT_LOAD>(xrow + cb + 8);
-            } else {
-                lo[u] = u32x4{0u, 0u, 0u, 0u};
-                hi[u] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    // the row loads do not depend on the slots and may start first (measured
-    // slightly slower at the V3 shape, so off by default)
-#if EP_DISPATCH_LOAD_FIRST
-    load_steps(i_begin);
-#endif
     const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
     int sk[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         sk[k] = k < a.K ? readlane(s_own, k) : -1;
-
-    for (int i0 = i_begin; i0 < i_end; i0 += kDispatchUnroll) {
-        if (i0 != i_begin || !EP_DISPATCH_LOAD_FIRST)
-            load_steps(i0);
-#pragma unroll
-        for (int u = 0; u < kDispatchUnroll; ++u) {
-            const int cb = (i0 + u) * kFp8ChPerIter + lane * 16;
-            const bool active = (i0 + u < i_end) && cb < H;
-            if (i0 + u >= i_end)
-                break;
-            float v[16];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[2 * j] = bf16_lo(lo[u][j]);
-                v[2 * j + 1] = bf16_hi(lo[u][j]);
-                v[8 + 2 * j] = bf16_lo(hi[u][j]);
-                v[8 + 2 * j + 1] = bf16_hi(hi[u][j]);
-            }
-            float m = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                m = fmaxf(m, fabsf(v[j]));
-            // 8 lanes hold one 128-channel block
-            m = fmaxf(m, __shfl_xor(m, 1));
-            m = fmaxf(m, __shfl_xor(m, 2));
-            m = fmaxf(m, __shfl_xor(m, 4));
-            const float amax = fmaxf(m, 0x1p-64f);
-            const float inv = 448.0f / amax;
-            const float scale = amax / 448.0f;
-            u32x4 q;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                q[j] = f32_to_e4m3fn(v[4 * j] * inv) | (f32_to_e4m3fn(v[4 * j + 1] * inv) << 8) |
-                       (f32_to_e4m3fn(v[4 * j + 2] * inv) << 16) | (f32_to_e4m3fn(v[4 * j + 3] * inv) << 24);
-            }
-            if (active) {
-                const int blk = cb / kQBlock;
-#pragma unroll
-                for (int k = 0; k < KMAX; ++k) {
-                    if (sk[k] >= 0) {
-                        store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, q);
-                        if ((lane & 7) == 0)
-                            a.scales[(size_t)sk[k] * nb + blk] = scale;
-                    }
-                }
-            }
-        }
-    }
+    const int i_begin = seg * a.iters_per_seg;
+    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
+    fp8_rows<KMAX>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end,
+                   static_cast<uint8_t*>(a.recv), a.scales);
 }
 
 template <int KMAX, bool FRESH>
@@ -200,47 +94,15 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_bf16_kernel(D
     const int seg = wi % a.nseg;
     if (t >= a.T)
         return;
-    const int lane = lane_id();
-    const int H = a.H;
-    const uint16_t* xrow = a.x + (size_t)t * H;
-    uint16_t* recv = static_cast<uint16_t*>(a.recv);
-    const int i_begin = seg * a.iters_per_seg;
-    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
-
-    u32x4 d[kDispatchUnroll];
-    auto load_steps = [&](int i0) {
-#pragma unroll
-        for (int u = 0; u < kDispatchUnroll; ++u) {
-            const int cb = (i0 + u) * kBf16ChPerIter + lane * 8;
-            if (i0 + u < i_end && cb < H)
-                d[u] = load16_hint<EP_DISPATCH_NT_LOAD>(xrow + cb);
-        }
-    };
-    // the row loads do not depend on the slots and may start first (measured
-    // slightly slower at the V3 shape, so off by default)
-#if EP_DISPATCH_LOAD_FIRST
-    load_steps(i_begin);
-#endif
     const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
     int sk[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         sk[k] = k < a.K ? readlane(s_own, k) : -1;
-
-    for (int i0 = i_begin; i0 < i_end; i0 += kDispatchUnroll) {
-        if (i0 != i_begin || !EP_DISPATCH_LOAD_FIRST)
-            load_steps(i0);
-#pragma unroll
-        for (int u = 0; u < kDispatchUnroll; ++u) {
-            const int cb = (i0 + u) * kBf16ChPerIter + lane * 8;
-            if (i0 + u < i_end && cb < H) {
-#pragma unroll
-                for (int k = 0; k < KMAX; ++k)
-                    if (sk[k] >= 0)
-                        store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, d[u]);
-            }
-        }
-    }
+    const int i_begin = seg * a.iters_per_seg;
+    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
+    bf16_rows<KMAX>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end,
+                    static_cast<uint16_t*>(a.recv));
 }
 
 hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)

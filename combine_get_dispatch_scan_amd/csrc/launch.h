@@ -34,6 +34,29 @@ struct DispatchLaunch {
 
 hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream);
 
+// Low-latency dispatch: T <= 256 tokens, static per-expert capacity `cap`.
+constexpr int kLowLatencyMaxTokens = 256;
+
+struct LowLatencyLaunch {
+    const void* x;
+    const int64_t* topk_idx;
+    const float* w_in;
+    int T, H, K, E, P, cap;
+    int use_fp8;
+    void* recv;
+    float* scales;
+    int32_t* slot;
+    float* w_copy;
+    int32_t* status;
+    int32_t* expert_offset;
+    int32_t* num_tokens_per_expert;
+    int32_t* num_tokens_per_partition;
+    uint8_t* is_token_in_partition;
+    int32_t* num_invalid;
+};
+
+hipError_t launch_low_latency_dispatch(const LowLatencyLaunch& L, hipStream_t stream);
+
 // combine; w == nullptr means unit weights (the backward of dispatch).
 hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
                           const float* w, void* out, hipStream_t stream);

@@ -60,6 +60,8 @@ extern "C" {
 #define EP_MAX_PARTITIONS  64
 #define EP_MAX_HIDDEN      32768
 
+#define EP_MAX_LL_TOKENS   256     /* tokens per ep_low_latency_dispatch call     */
+
 #define EP_HANDLE_MAGIC    0x31485045u   /* "EPH1" */
 
 /*
@@ -81,12 +83,14 @@ typedef struct ep_handle {
     int32_t  capacity_rows;    /* rows available in recv_x (set by ep_dispatch)    */
     int32_t  has_weights;      /* 1 when ep_dispatch copied topk_weights            */
     int32_t  num_chunks;       /* ceil(T / 256)                                    */
-    int32_t  reserved;
+    int32_t  static_cap;       /* rows per expert of ep_low_latency_dispatch's
+                                  static layout; 0 for the dense layout          */
     void*    ws;               /* the workspace                                    */
     size_t   ws_bytes;
     int32_t* expert_offset;    /* [E+1] first receive row of each expert; [E] = N  */
     int32_t* slot;             /* [T*K] receive row of pair (t,k), -1 if none      */
-    int32_t* src_token;        /* [T*K] source token of receive row r, r < min(N, capacity) */
+    int32_t* src_token;        /* [T*K] source token of receive row r, r < min(N, capacity);
+                                  NULL for the static layout                     */
     float*   weights;          /* [T*K] copy of topk_weights                       */
     int32_t* status;           /* [4] overflow flag, num_invalid, N, 0             */
     int32_t* pair_code;        /* [T*K] (expert << 8 | rank in chunk), -1 if none  */
@@ -158,6 +162,42 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int num_tokens, int num_topk
 int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp8,
                 void* recv_x, float* recv_scales, int capacity_rows,
                 ep_handle_t* handle, hipStream_t stream);
+
+/*
+ * Low-latency dispatch for decode batches: layout, slot assignment and the
+ * (quantise-and-)permute in ONE kernel launch, with no host synchronisation
+ * and no memset, so it can be captured in a HIP graph (devtrends.ru "Как это
+ * выглядит в коде": low_latency_dispatch(hidden_states, topk_idx,
+ * num_max_tokens, num_experts); stakiran summary section 3: the decode path,
+ * CUDA-graph compatible).  The receive buffer has a static per-expert
+ * capacity: expert e owns rows [e*cap, (e+1)*cap), and a dispatched pair takes
+ * row e*cap + (its rank among expert e's pairs in token order).  A pair whose
+ * rank reaches cap is dropped (slot -1) and flagged.  Rows past an expert's
+ * count are not written.
+ *
+ *   x, topk_idx, topk_weights   as for ep_get_dispatch_layout / ep_dispatch;
+ *                               1 <= num_tokens <= EP_MAX_LL_TOKENS (0 allowed)
+ *   num_max_tokens              cap, rows per expert (E*cap < 2^31)
+ *   recv_x                      bf16 or e4m3fn [E*cap*H]; recv_scales fp32
+ *                               [E*cap*H/128] in FP8 mode
+ *   num_tokens_per_expert ...   the layout outputs, as ep_get_dispatch_layout
+ *                               (num_tokens_per_expert counts every dispatched
+ *                               pair, including dropped ones)
+ *   ws, ws_bytes                ep_workspace_bytes(T, K, E, P)
+ *   handle                      out: a dispatched handle.  ep_combine,
+ *                               ep_dispatch_cached and the backward calls use
+ *                               it as any other; ep_handle_recv_counts reports
+ *                               min(count, cap) rows per expert and returns
+ *                               EP_ECAPACITY when a pair was dropped.
+ * Errors: EP_EINVAL, EP_EHIP.
+ */
+int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                            int num_tokens, int hidden, int num_topk, int num_experts,
+                            int num_partitions, int use_fp8, int num_max_tokens,
+                            void* recv_x, float* recv_scales,
+                            int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_partition, int32_t* num_invalid,
+                            void* ws, size_t ws_bytes, ep_handle_t* handle, hipStream_t stream);
 
 /*
  * Cached dispatch: re-sends new token rows along the routing of an earlier

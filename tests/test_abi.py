@@ -209,3 +209,59 @@ def test_backward_calls_validate_before_any_hip_call():
     assert ep.ep_combine_backward(FAKE, None, h2, FAKE, FAKE, FAKE, None) == ep.EP_EINVAL
     assert "needs y" in ep.ep_last_error()
     assert ep.ep_combine_backward(FAKE, FAKE, h2, FAKE, FAKE, FAKE + 2, None) == ep.EP_EINVAL
+
+
+def _ll_args(**kw):
+    T, K, E, P = 32, 4, 16, 4
+    a = dict(x=FAKE, topk_idx=FAKE, topk_weights=FAKE, num_tokens=T, hidden=256, num_topk=K,
+             num_experts=E, num_partitions=P, use_fp8=1, num_max_tokens=8, recv_x=FAKE,
+             recv_scales=FAKE, num_tokens_per_partition=FAKE, num_tokens_per_expert=FAKE,
+             is_token_in_partition=FAKE, num_invalid=FAKE, ws=FAKE,
+             ws_bytes=ep.ep_workspace_bytes(T, K, E, P), handle=ep.ep_handle_t(), stream=None)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(num_tokens=257), "at most 256"),
+    (dict(num_tokens=-1), "invalid dims"),
+    (dict(num_max_tokens=0), "num_max_tokens"),
+    (dict(num_max_tokens=1 << 30), "num_max_tokens"),
+    (dict(num_experts=15), "invalid dims"),
+    (dict(topk_idx=None), "topk_idx"),
+    (dict(topk_idx=FAKE + 4), "topk_idx"),
+    (dict(is_token_in_partition=None), "is_token_in_partition"),
+    (dict(num_invalid=None), "count outputs"),
+    (dict(topk_weights=FAKE + 2), "topk_weights"),
+    (dict(ws=FAKE + 16), "workspace"),
+    (dict(ws_bytes=64), "workspace too small"),
+    (dict(hidden=100), "hidden"),
+    (dict(hidden=136), "hidden % 128"),
+    (dict(use_fp8=2), "use_fp8"),
+    (dict(x=None), "x must"),
+    (dict(recv_x=FAKE + 8), "recv_x"),
+    (dict(recv_scales=None), "recv_scales"),
+    (dict(handle=None), "handle"),
+])
+def test_low_latency_dispatch_rejects_invalid_arguments(kw, msg):
+    a = _ll_args(**kw)
+    h = a["handle"]
+    if a["handle"] is None:
+        rc = ep.load().ep_low_latency_dispatch(*[a[k] for k in list(a)[:-2]], None, None)
+    else:
+        rc = ep.ep_low_latency_dispatch(**a)
+    assert rc == ep.EP_EINVAL, ep.ep_last_error()
+    assert msg in ep.ep_last_error(), ep.ep_last_error()
+    if h is not None:
+        assert h.magic == 0, "handle written on an error path"
+
+
+def test_static_handle_is_refused_by_fresh_dispatch():
+    h = _fake_handle(stage=2)
+    h.static_cap = 8
+    rc = ep.ep_dispatch(FAKE, FAKE, 256, 1, FAKE, FAKE, 16 * 8, h, None)
+    assert rc == ep.EP_EINVAL and "ep_dispatch_cached" in ep.ep_last_error()
+    # the cached call accepts E*cap rows for a static handle, and no more
+    h.capacity_rows = 16 * 8 + 1
+    assert ep.ep_dispatch_cached(FAKE, h, FAKE, FAKE, None) == ep.EP_EINVAL
+    assert "capacity_rows" in ep.ep_last_error()
