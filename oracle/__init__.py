@@ -66,6 +66,8 @@ def lib():
         L.oracle_dispatch.restype = None
         L.oracle_combine.argtypes = [P, i32, i32, i32, P, P, P]
         L.oracle_combine.restype = None
+        L.oracle_combine_fp8.argtypes = [P, P, i32, i32, i32, P, P, P]
+        L.oracle_combine_fp8.restype = None
         L.oracle_dispatch_backward.argtypes = [P, i32, i32, i32, P, P]
         L.oracle_dispatch_backward.restype = None
         L.oracle_combine_backward.argtypes = [P, P, i32, i32, i32, P, P, P, P]
@@ -200,6 +202,20 @@ def combine(y_bits: np.ndarray, slot: np.ndarray, w: np.ndarray) -> np.ndarray:
     H = y.shape[1]
     out = np.empty((T, H), np.uint16)
     lib().oracle_combine(_p(y), T, H, K, _p(slot), _p(w), _p(out))
+    return out
+
+
+def combine_fp8(q: np.ndarray, scales: np.ndarray, slot: np.ndarray, w) -> np.ndarray:
+    """Combine of FP8 rows (codes uint8 [rows,H], scales fp32 [rows,H/128]);
+    w None = unit weights.  Returns bf16 bits [T,H]."""
+    q = _c(q, np.uint8)
+    sc = _c(scales, np.float32)
+    slot = _c(slot, np.int32)
+    T, K = slot.shape
+    H = q.shape[1]
+    wv = None if w is None else _c(w, np.float32)
+    out = np.empty((T, H), np.uint16)
+    lib().oracle_combine_fp8(_p(q), _p(sc), T, H, K, _p(slot), None if wv is None else _p(wv), _p(out))
     return out
 
 

@@ -308,6 +308,31 @@ void oracle_combine(const uint16_t* y, int T, int H, int K, const int32_t* slot,
     }
 }
 
+/* Combine of FP8 rows (the dequantising option of the backward of dispatch,
+ * and of combine): each received element is first widened to its value,
+ * v = decode(q) * scale of its 128-channel block (one fp32 multiply), then
+ * reduced as in oracle_combine.  w == NULL means unit weights, for which
+ * fmaf(1, v, acc) is the plain sum acc + v. */
+void oracle_combine_fp8(const uint8_t* q, const float* scales, int T, int H, int K,
+                        const int32_t* slot, const float* w, uint16_t* out)
+{
+    const int nb = H / 128;
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < H; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int32_t r = slot[(size_t)t * K + k];
+                if (r < 0)
+                    continue;
+                float v = oracle_e4m3fn_to_f32(q[(size_t)r * H + j]) * scales[(size_t)r * nb + j / 128];
+                float wk = w ? w[(size_t)t * K + k] : 1.0f;
+                acc = fmaf(wk, v, acc);
+            }
+            out[(size_t)t * H + j] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
 /* Backward of dispatch (straight-through for the FP8 cast): each token's
  * gradient is the sum of the gradients of its received rows.  The sum is the
  * combine definition with unit weights: fp32, k ascending, from +0.0f, then

@@ -82,6 +82,13 @@ void oracle_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* slot
 void oracle_combine(const uint16_t* y, int T, int H, int K, const int32_t* slot,
                     const float* w, uint16_t* out);
 
+/* Combine of FP8 rows q [rows, H] with fp32 block scales [rows, H/128]:
+ *   v = e4m3fn_to_f32(q) * scale   (one fp32 multiply)
+ *   out[t, j] = bf16_rne( fmaf chain over k ascending of w[t,k] * v, from +0.0f )
+ * w == NULL: unit weights (the dequantising backward of dispatch). */
+void oracle_combine_fp8(const uint8_t* q, const float* scales, int T, int H, int K,
+                        const int32_t* slot, const float* w, uint16_t* out);
+
 /* Backward of dispatch: the backward of dispatch is combine (stakiran summary,
  * section 3).  With the FP8 cast taken as straight-through, grad_x[t] =
  * bf16_rne( fp32 sum over dispatched k ascending of grad_recv[slot[t,k]],

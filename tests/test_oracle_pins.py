@@ -597,3 +597,75 @@ def test_static_slots_against_stable_sort(T, E, K, cap, mode):
     s = slot[slot >= 0]
     assert np.unique(s).size == s.size
     assert np.all(s // cap == idx[slot >= 0])
+
+
+# ----------------------------------------------------------------------------
+# combine of FP8 rows (the dequantising option of the backward of dispatch)
+# ----------------------------------------------------------------------------
+
+def _finite_codes(rng, shape):
+    q = rng.integers(0, 256, shape, dtype=np.uint32).astype(np.uint8)
+    nan = (q & 0x7F) == 0x7F
+    q[nan] ^= 0x01                       # 0x7F / 0xFF (NaN) -> 0x7E / 0xFE (+-448)
+    return q
+
+
+def test_combine_fp8_single_pair_matches_torch_dequant():
+    """K=1, unit weight: out = bf16( +0 + decode(q) * scale ), with torch's own
+    float8_e4m3fn decoder, fp32 multiply and bfloat16 rounding (the sum starts
+    from +0, so a -0 product gives +0)."""
+    rng = np.random.default_rng(31)
+    T, H = 64, 256
+    q = _finite_codes(rng, (T, H))
+    sc = (rng.standard_normal((T, H // 128)).astype(np.float32) *
+          np.ldexp(np.float32(1), rng.integers(-20, 21, (T, H // 128))).astype(np.float32))
+    slot = rng.permutation(T).astype(np.int32).reshape(T, 1)
+    out = oracle.combine_fp8(q, sc, slot, None)
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).float()
+    s_full = torch.from_numpy(np.repeat(sc, 128, axis=1))
+    want = ((dec * s_full)[torch.from_numpy(slot[:, 0].astype(np.int64))] + 0.0).to(torch.bfloat16)
+    assert np.array_equal(out, want.view(torch.int16).numpy().view(np.uint16))
+    # weighted form with w = 1 is the unit form
+    assert np.array_equal(oracle.combine_fp8(q, sc, slot, np.ones((T, 1), np.float32)), out)
+
+
+def test_combine_fp8_pow2_scales_and_weights_exact():
+    """Power-of-two scales and weights keep every product and partial sum a
+    short dyadic number: the fp32 chain is exact and only the final rounding
+    (torch's bf16 RNE of the exact sum) remains."""
+    T, H, E, K = 48, 256, 16, 4
+    idx, w = workloads.random_case(32, T, E, K, weights="pow2", mask_frac=0.1)
+    r = _pipeline(idx, w, None, E, 4, False)
+    rng = np.random.default_rng(33)
+    rows = r["rows"]
+    q = _finite_codes(rng, (rows, H))
+    q[(q & 0x78) > 0x50] &= 0x87         # keep magnitudes < 2^4 so sums stay short
+    sc = np.ldexp(np.float32(1), rng.integers(-6, 3, (rows, H // 128))).astype(np.float32)
+    out = _f32(oracle.combine_fp8(q, sc, r["slot"], w)).astype(np.float64)
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    v = dec * np.repeat(sc.astype(np.float64), 128, axis=1)
+    exact = np.zeros((T, H))
+    for t in range(T):
+        for k in range(K):
+            s = r["slot"][t, k]
+            if s >= 0:
+                exact[t] += float(w[t, k]) * v[s]
+    ref = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(out, ref.astype(np.float64))
+    # a token whose every pair is masked gets +0
+    dead = np.all(r["slot"] < 0, axis=1)
+    assert np.all(oracle.combine_fp8(q, sc, r["slot"], w)[dead] == 0)
+
+
+def test_combine_fp8_round_trip_within_fp8_error():
+    """dispatch (FP8) then the FP8 combine with unit weights: each token's K
+    identical rows sum to K * x within the FP8 error bound."""
+    wl = workloads.config("decode")
+    idx, w, x = workloads.make(wl)
+    r = _pipeline(idx, w, x, wl.E, wl.P, True)
+    out = _f32(oracle.combine_fp8(r["recv_x"], r["recv_scales"], r["slot"], None)).astype(np.float64)
+    xf = _f32(x).astype(np.float64)
+    kk = (r["slot"] >= 0).sum(axis=1, keepdims=True).astype(np.float64)
+    s_tok = np.repeat(r["recv_scales"][np.maximum(r["slot"][:, 0], 0)], 128, axis=1)
+    bound = kk * (2.0 ** -4 * np.abs(xf) + 2.0 ** -10 * s_tok) + 2.0 ** -8 * kk * np.abs(xf) + 1e-30
+    assert np.all(np.abs(out - kk * xf) <= bound)
