@@ -426,6 +426,12 @@ def main():
         "combine_backward_us": round(cb_ms * 1e3, 2),
         "combine_backward_hbm_frac": round(cb_bytes / (cb_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
     }
+    if wl.use_fp8:
+        # the dequantising backward of dispatch, on FP8 rows + scales (here dispatch's own)
+        d8_ms = time_call(lambda: _ok(ep.ep_dispatch_backward_fp8(p(recv), p(scales), h, p(grad_x), sp)))
+        d8_bytes = N * H + N * (H // 128) * 4 + T * H * 2 + T * K * 4
+        backward["dispatch_backward_fp8_us"] = round(d8_ms * 1e3, 2)
+        backward["dispatch_backward_fp8_hbm_frac"] = round(d8_bytes / (d8_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
     del grad_x, grad_y, grad_w
 
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)

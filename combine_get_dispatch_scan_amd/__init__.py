@@ -82,6 +82,8 @@ _SIGS = {
                                 ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_dispatch": ([_P, _P, _I, _I, _P, _P, _I, ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_dispatch_cached": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_combine_fp8": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_dispatch_backward_fp8": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P], _I),
     "ep_low_latency_dispatch": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                                  _P, ctypes.c_size_t, ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_combine": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
@@ -165,6 +167,15 @@ def ep_dispatch_cached(x, handle, recv_x, recv_scales, stream) -> int:
 
 def ep_combine(y, handle, topk_weights, out, stream) -> int:
     return load().ep_combine(y, ctypes.byref(handle), topk_weights, out, stream)
+
+
+def ep_combine_fp8(y, y_scales, handle, topk_weights, out, stream) -> int:
+    return load().ep_combine_fp8(y, y_scales, ctypes.byref(handle), topk_weights, out, stream)
+
+
+def ep_dispatch_backward_fp8(grad_recv, grad_scales, handle, grad_x, stream) -> int:
+    return load().ep_dispatch_backward_fp8(grad_recv, grad_scales, ctypes.byref(handle), grad_x,
+                                           stream)
 
 
 def ep_dispatch_backward(grad_recv, handle, grad_x, stream) -> int:
@@ -367,6 +378,28 @@ def combine(y, handle: Handle, topk_weights=None, out=None):
         out = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=y.device)
     _check(ep_combine(_ptr(y), c, _ptr(topk_weights), _ptr(out), _stream()))
     return out
+
+
+def combine_fp8(y, y_scales, handle: Handle, topk_weights=None, out=None):
+    """y: float8_e4m3fn (or uint8) [rows, H] with fp32 scales [rows, H/128], in
+    dispatch's receive order.  Returns bf16 [T, H]."""
+    import torch
+    c = handle.c
+    if out is None:
+        out = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=y.device)
+    _check(ep_combine_fp8(_ptr(y), _ptr(y_scales), c, _ptr(topk_weights), _ptr(out), _stream()))
+    return out
+
+
+def dispatch_backward_fp8(grad_recv, grad_scales, handle: Handle, grad_x=None):
+    """grad_recv: float8_e4m3fn [rows, H] + fp32 scales [rows, H/128].
+    Returns grad_x bf16 [T, H]."""
+    import torch
+    c = handle.c
+    if grad_x is None:
+        grad_x = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=grad_recv.device)
+    _check(ep_dispatch_backward_fp8(_ptr(grad_recv), _ptr(grad_scales), c, _ptr(grad_x), _stream()))
+    return grad_x
 
 
 def dispatch_backward(grad_recv, handle: Handle, grad_x=None):

@@ -395,6 +395,56 @@ int ep_dispatch_backward(const void* grad_recv, const ep_handle_t* handle, void*
     return EP_OK;
 }
 
+static int run_combine_fp8(const void* y, const float* y_scales, const ep_handle_t* handle,
+                           const float* w, void* out, const char* what, hipStream_t stream)
+{
+    const int T = handle->num_tokens;
+    const int H = handle->hidden;
+    if (H % 128 != 0)
+        return fail(EP_EINVAL, "FP8 rows need hidden %% 128 == 0 (hidden=%d)", H);
+    if (T > 0 && (!out || !aligned(out, 16)))
+        return fail(EP_EINVAL, "%s must be a non-NULL 16-byte aligned device pointer",
+                    w ? "out" : "grad_x");
+    if (T > 0 && handle->capacity_rows > 0 && (!y || !aligned(y, 16)))
+        return fail(EP_EINVAL, "the FP8 rows must be a non-NULL 16-byte aligned device pointer");
+    if (T > 0 && handle->capacity_rows > 0 && (!y_scales || !aligned(y_scales, 4)))
+        return fail(EP_EINVAL, "the FP8 scales must be a non-NULL 4-byte aligned device pointer");
+    hipError_t e = moe_ep::launch_combine_fp8(y, y_scales, T, H, handle->num_topk, handle->slot, w,
+                                              out, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, what);
+    return EP_OK;
+}
+
+int ep_combine_fp8(const void* y, const float* y_scales, const ep_handle_t* handle,
+                   const float* topk_weights, void* out, hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 2);
+    if (rc)
+        return rc;
+    const int T = handle->num_tokens;
+    const float* w = topk_weights ? topk_weights : (handle->has_weights ? handle->weights : nullptr);
+    if (!w && T > 0)
+        return fail(EP_EINVAL, "no weights: pass topk_weights or give them to ep_dispatch");
+    if (w && !aligned(w, 4))
+        return fail(EP_EINVAL, "topk_weights must be 4-byte aligned");
+    if (!w)                       // T == 0: nothing is launched; any non-null marks "weighted"
+        w = handle->weights;
+    return run_combine_fp8(y, y_scales, handle, w, out, "FP8 combine launch", stream);
+}
+
+int ep_dispatch_backward_fp8(const void* grad_recv, const float* grad_scales,
+                             const ep_handle_t* handle, void* grad_x, hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(handle, 2);
+    if (rc)
+        return rc;
+    return run_combine_fp8(grad_recv, grad_scales, handle, nullptr, grad_x,
+                           "FP8 dispatch backward launch", stream);
+}
+
 int ep_combine_backward(const void* grad_out, const void* y, const ep_handle_t* handle,
                         const float* topk_weights, void* grad_y, float* grad_w,
                         hipStream_t stream)

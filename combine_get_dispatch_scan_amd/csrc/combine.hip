@@ -126,6 +126,150 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
     }
 }
 
+// Combine of FP8 rows: every gathered element is first widened to
+// decode(q) * (its block's scale), one fp32 multiply, then reduced as above.
+// Each lane owns 16 channels (one 16-byte load per row) per wave step of 1024
+// channels; its 8-lane group shares one 128-channel block, so one scale per
+// row; the 16 BF16 results leave as two 16-byte stores.
+struct CombineFp8Args {
+    const uint8_t* y;
+    const float* scales;
+    int T, H, K;
+    int nseg, iters_per_seg, iters;
+    const int32_t* slot;
+    const float* w;
+    uint16_t* out;
+};
+
+#ifndef EP_COMBINE_FP8_UNROLL
+#define EP_COMBINE_FP8_UNROLL 1
+#endif
+#ifndef EP_COMBINE_FP8_MAX_ITERS
+#define EP_COMBINE_FP8_MAX_ITERS 4
+#endif
+// Measured at the V3 shape (dispatch backward on dispatch's own FP8 rows):
+// plain write-back stores 122 us, write-through (sc1) 128 us; two wave steps
+// in flight per wave 133 us; plain loads of the rows 156 us.
+#ifndef EP_COMBINE_FP8_STORE_AUX
+#define EP_COMBINE_FP8_STORE_AUX 0
+#endif
+constexpr int kCombineFp8ChPerIter = kWave * 16;   // 1024 channels per wave step
+constexpr int kCombineFp8Unroll = EP_COMBINE_FP8_UNROLL;
+
+template <int KMAX, bool UNIT>
+__global__ __launch_bounds__(kCombineWaves * kWave) void combine_fp8_kernel(CombineFp8Args a)
+{
+    const int wi = blockIdx.x * kCombineWaves + threadIdx.x / kWave;
+    const int t = wi / a.nseg;
+    const int seg = wi % a.nseg;
+    if (t >= a.T)
+        return;
+    const int lane = lane_id();
+    int s_own = -1;
+    float w_own = 0.0f;
+    if (lane < a.K) {
+        s_own = a.slot[(size_t)t * a.K + lane];
+        w_own = UNIT ? 1.0f : a.w[(size_t)t * a.K + lane];
+    }
+    int sk[KMAX];
+    float wk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+        wk[k] = k < a.K ? readlane_f(w_own, k) : 0.0f;
+    }
+
+    const int H = a.H;
+    const int nb = H / kQBlock;
+    const __amdgpu_buffer_rsrc_t orow = make_rsrc(a.out + (size_t)t * H, H * 2);
+    const int i_begin = seg * a.iters_per_seg;
+    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
+
+    for (int i0 = i_begin; i0 < i_end; i0 += kCombineFp8Unroll) {
+        u32x4 d[kCombineFp8Unroll][KMAX];
+        float sc[kCombineFp8Unroll][KMAX];
+#pragma unroll
+        for (int u = 0; u < kCombineFp8Unroll; ++u) {
+            const int cb = (i0 + u) * kCombineFp8ChPerIter + lane * 16;
+            const bool active = (i0 + u < i_end) && cb < H;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (sk[k] >= 0 && active) {
+                    d[u][k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk[k] * H + cb);
+                    sc[u][k] = a.scales[(size_t)sk[k] * nb + cb / kQBlock];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineFp8Unroll; ++u) {
+            const int cb = (i0 + u) * kCombineFp8ChPerIter + lane * 16;
+            const bool active = (i0 + u < i_end) && cb < H;
+            float acc[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (sk[k] >= 0 && active) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float v[4];
+                        e4m3fn_pair_to_f32<false>(d[u][k][j], v[0], v[1]);
+                        e4m3fn_pair_to_f32<true>(d[u][k][j], v[2], v[3]);
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            acc[4 * j + b] = __builtin_fmaf(wk[k], v[b] * sc[u][k], acc[4 * j + b]);
+                    }
+                }
+            }
+            if (active) {
+                u32x4 o0, o1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o0[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+                    o1[j] = pack_bf16x2(acc[8 + 2 * j], acc[8 + 2 * j + 1]);
+                }
+                buffer_store16<EP_COMBINE_FP8_STORE_AUX>(o0, orow, cb * 2);
+                buffer_store16<EP_COMBINE_FP8_STORE_AUX>(o1, orow, cb * 2 + 16);
+            }
+        }
+    }
+}
+
+hipError_t launch_combine_fp8(const void* y, const float* scales, int T, int H, int K,
+                              const int32_t* slot, const float* w, void* out, hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    CombineFp8Args a;
+    a.y = static_cast<const uint8_t*>(y);
+    a.scales = scales;
+    a.T = T;
+    a.H = H;
+    a.K = K;
+    a.slot = slot;
+    a.w = w;
+    a.out = static_cast<uint16_t*>(out);
+    a.iters = (H + kCombineFp8ChPerIter - 1) / kCombineFp8ChPerIter;
+    const RowSplit rs = split_rows(T, a.iters, EP_COMBINE_MIN_ITEMS, EP_COMBINE_FP8_MAX_ITERS);
+    a.nseg = rs.nseg;
+    a.iters_per_seg = rs.iters_per_seg;
+    const long long items = (long long)T * a.nseg;
+    dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
+    dim3 block(kCombineWaves * kWave);
+#define EP_COMBINE8(KM)                                                                          \
+    do {                                                                                         \
+        if (w) hipLaunchKernelGGL((combine_fp8_kernel<KM, false>), grid, block, 0, stream, a);   \
+        else hipLaunchKernelGGL((combine_fp8_kernel<KM, true>), grid, block, 0, stream, a);      \
+    } while (0)
+    if (K <= 2) EP_COMBINE8(2);
+    else if (K <= 4) EP_COMBINE8(4);
+    else if (K <= 8) EP_COMBINE8(8);
+    else EP_COMBINE8(16);
+#undef EP_COMBINE8
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
                           const float* w, void* out, hipStream_t stream)
 {

@@ -132,4 +132,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float v)
     return sign | code;
 }
 
+// Two OCP E4M3FN codes (bytes 0,1 or, with HI, bytes 2,3 of w) -> their exact
+// fp32 values, with gfx950's converter (v_cvt_pk_f32_fp8).  It decodes the OCP
+// format exactly -- subnormals m * 2^-9, 0x7F / 0xFF as NaN -- which a device
+// test checks against the formula on all 256 codes.
+template <bool HI>
+__device__ __forceinline__ void e4m3fn_pair_to_f32(uint32_t w, float& a, float& b)
+{
+    const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+    a = v[0];
+    b = v[1];
+}
+
 }  // namespace moe_ep

@@ -61,6 +61,10 @@ hipError_t launch_low_latency_dispatch(const LowLatencyLaunch& L, hipStream_t st
 hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
                           const float* w, void* out, hipStream_t stream);
 
+// combine of FP8 rows with fp32 block scales (w == nullptr: unit weights).
+hipError_t launch_combine_fp8(const void* y, const float* scales, int T, int H, int K,
+                              const int32_t* slot, const float* w, void* out, hipStream_t stream);
+
 // backward of combine: grad_y rows (and grad_w when y != nullptr).
 hipError_t launch_combine_backward(const void* grad_out, const void* y, int T, int H, int K,
                                    const int32_t* slot, const float* w, void* grad_y,

@@ -239,6 +239,25 @@ int ep_dispatch_backward(const void* grad_recv, const ep_handle_t* handle, void*
                          hipStream_t stream);
 
 /*
+ * Combine and backward of dispatch on FP8 rows: the dequantising option of
+ * the backward of dispatch (stakiran summary, section 3: the backward of
+ * dispatch is combine), for rows that arrive as E4M3FN codes with the same
+ * per-128-channel fp32 scales dispatch produces (aikraft.ru "Технические
+ * детали и требования": FP8 traffic).  Each gathered element is widened to
+ * decode(q) * scale (one fp32 multiply) and then reduced as in ep_combine
+ * (weighted) or ep_dispatch_backward (unit weights).
+ *   y / grad_recv          device e4m3fn [capacity_rows*H], receive order
+ *   y_scales / grad_scales device fp32 [capacity_rows*H/128]
+ *   topk_weights           as for ep_combine
+ *   out / grad_x           device bf16 [T*H]
+ * Needs hidden % 128 == 0.  Errors: EP_EINVAL, EP_EHIP.
+ */
+int ep_combine_fp8(const void* y, const float* y_scales, const ep_handle_t* handle,
+                   const float* topk_weights, void* out, hipStream_t stream);
+int ep_dispatch_backward_fp8(const void* grad_recv, const float* grad_scales,
+                             const ep_handle_t* handle, void* grad_x, hipStream_t stream);
+
+/*
  * Backward of combine: the backward of combine is dispatch (same passages),
  * of grad_out scaled by each pair's weight, plus the weight gradient:
  *   grad_y[slot[t,k]] = bf16_rne(w[t,k] * grad_out[t])   (one fp32 product)

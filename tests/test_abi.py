@@ -265,3 +265,25 @@ def test_static_handle_is_refused_by_fresh_dispatch():
     h.capacity_rows = 16 * 8 + 1
     assert ep.ep_dispatch_cached(FAKE, h, FAKE, FAKE, None) == ep.EP_EINVAL
     assert "capacity_rows" in ep.ep_last_error()
+
+
+def test_fp8_combine_calls_validate_before_any_hip_call():
+    h1 = _fake_handle(stage=1)
+    assert ep.ep_combine_fp8(FAKE, FAKE, h1, FAKE, FAKE, None) == ep.EP_EINVAL
+    assert ep.ep_dispatch_backward_fp8(FAKE, FAKE, h1, FAKE, None) == ep.EP_EINVAL
+    h2 = _fake_handle(stage=2)
+    for args, msg in [((FAKE + 8, FAKE, h2, FAKE, FAKE), "FP8 rows"),
+                      ((FAKE, None, h2, FAKE, FAKE), "FP8 scales"),
+                      ((FAKE, FAKE + 2, h2, FAKE, FAKE), "FP8 scales"),
+                      ((FAKE, FAKE, h2, FAKE, FAKE + 8), "out"),
+                      ((FAKE, FAKE, h2, FAKE + 2, FAKE), "topk_weights")]:
+        assert ep.ep_combine_fp8(*args, None) == ep.EP_EINVAL
+        assert msg in ep.ep_last_error(), (msg, ep.ep_last_error())
+    h2.has_weights = 0
+    assert ep.ep_combine_fp8(FAKE, FAKE, h2, None, FAKE, None) == ep.EP_EINVAL
+    assert "no weights" in ep.ep_last_error()
+    assert ep.ep_dispatch_backward_fp8(FAKE, FAKE, h2, FAKE + 8, None) == ep.EP_EINVAL
+    assert "grad_x" in ep.ep_last_error()
+    h2.hidden = 136
+    assert ep.ep_dispatch_backward_fp8(FAKE, FAKE, h2, FAKE, None) == ep.EP_EINVAL
+    assert "hidden % 128" in ep.ep_last_error()
