@@ -58,6 +58,10 @@ def lib():
         L.oracle_layout.restype = i32
         L.oracle_expert_offsets.argtypes = [P, i32, P]
         L.oracle_expert_offsets.restype = None
+        L.oracle_expert_offsets_aligned.argtypes = [P, i32, i32, P]
+        L.oracle_expert_offsets_aligned.restype = None
+        L.oracle_dispatch_fp8_input.argtypes = [P, P, i32, i32, i32, P, P, P]
+        L.oracle_dispatch_fp8_input.restype = None
         L.oracle_slots.argtypes = [P, P, i32, i32, P, i32, i32, P, P, P]
         L.oracle_slots.restype = None
         L.oracle_slots_static.argtypes = [P, P, i32, i32, i32, i32, P, P]
@@ -133,10 +137,15 @@ def layout(topk_idx: np.ndarray, E: int, P: int):
                 is_token_in_partition=mask, num_invalid=int(ninv[0]), valid=valid)
 
 
-def expert_offsets(cnt: np.ndarray) -> np.ndarray:
+def expert_offsets(cnt: np.ndarray, align: int = 1) -> np.ndarray:
+    """Exclusive prefix sum of the counts; align > 1 rounds each expert's block
+    up to a multiple of align (GEMM-aligned layout)."""
     cnt = _c(cnt, np.int32)
     off = np.empty(cnt.size + 1, np.int32)
-    lib().oracle_expert_offsets(_p(cnt), cnt.size, _p(off))
+    if align == 1:
+        lib().oracle_expert_offsets(_p(cnt), cnt.size, _p(off))
+    else:
+        lib().oracle_expert_offsets_aligned(_p(cnt), cnt.size, align, _p(off))
     return off
 
 
@@ -194,6 +203,20 @@ def dispatch(x_bits: np.ndarray, slot: np.ndarray, rows: int, use_fp8: bool):
     return recv, None
 
 
+def dispatch_fp8_input(xq: np.ndarray, xs: np.ndarray, slot: np.ndarray, rows: int):
+    """Pre-quantised rows: returns (recv uint8 [rows,H], scales fp32 [rows,H/128]),
+    rows no pair maps to left zero."""
+    xq = _c(xq, np.uint8)
+    xs = _c(xs, np.float32)
+    slot = _c(slot, np.int32)
+    T, H = xq.shape
+    K = slot.shape[1]
+    recv = np.zeros((rows, H), np.uint8)
+    scales = np.zeros((rows, H // 128), np.float32)
+    lib().oracle_dispatch_fp8_input(_p(xq), _p(xs), T, H, K, _p(slot), _p(recv), _p(scales))
+    return recv, scales
+
+
 def combine(y_bits: np.ndarray, slot: np.ndarray, w: np.ndarray) -> np.ndarray:
     y = _c(y_bits, np.uint16)
     slot = _c(slot, np.int32)
@@ -247,16 +270,18 @@ def combine_backward(grad_out_bits: np.ndarray, y_bits, slot: np.ndarray, w: np.
     return grad_y, grad_w
 
 
-def run_all(topk_idx, topk_weights, x_bits, E, P, use_fp8, capacity=None, y_bits=None):
+def run_all(topk_idx, topk_weights, x_bits, E, P, use_fp8, capacity=None, y_bits=None, align=1):
     """The whole path on the CPU: layout, offsets, slots, dispatch and, when
-    y_bits is given, combine.  Returns a dict of every intermediate."""
+    y_bits is given, combine.  Returns a dict of every intermediate.  With
+    align > 1 the receive layout is GEMM-aligned; the default capacity is then
+    the worst case T*K + E*(align-1)."""
     T, K = topk_idx.shape
     lay = layout(topk_idx, E, P)
-    off = expert_offsets(lay["num_tokens_per_expert"])
-    cap = T * K if capacity is None else capacity
+    off = expert_offsets(lay["num_tokens_per_expert"], align)
+    cap = T * K + E * (align - 1) if capacity is None else capacity
     slot, src, ovf = slots(topk_idx, lay["valid"], off, cap)
-    N = int(off[-1])
-    rows = min(N, cap)
+    N = int(lay["num_tokens_per_expert"].sum())        # dispatched pairs
+    rows = min(int(off[-1]), cap)                      # receive rows (padding included)
     res = dict(lay, expert_offset=off, slot=slot, src_token=src[:rows], overflow=ovf, N=N, rows=rows)
     if x_bits is not None:
         recv, scales = dispatch(x_bits, slot, rows, use_fp8)

@@ -190,6 +190,18 @@ void oracle_expert_offsets(const int32_t* num_tokens_per_expert, int E, int32_t*
         off[e + 1] = off[e] + num_tokens_per_expert[e];
 }
 
+/* GEMM-aligned variant: each expert's block of rows is its count rounded up
+ * to a multiple of A, so every block starts on a multiple of A (the grouped
+ * GEMM's row tile).  The rows of a block past its count are padding. */
+void oracle_expert_offsets_aligned(const int32_t* num_tokens_per_expert, int E, int A, int32_t* off)
+{
+    off[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int32_t c = num_tokens_per_expert[e];
+        off[e + 1] = off[e] + ((c + A - 1) / A) * A;
+    }
+}
+
 /* Every valid (token, k) pair gets one receive row.  Reading: rows of one
  * expert are ordered by ascending source token (a stable counting sort of the
  * pairs by expert id), which makes the assignment deterministic.  A pair whose
@@ -304,6 +316,24 @@ void oracle_combine(const uint16_t* y, int T, int H, int K, const int32_t* slot,
                 acc = fmaf(w[(size_t)t * K + k], oracle_bf16_to_f32(y[(size_t)r * H + j]), acc);
             }
             out[(size_t)t * H + j] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
+/* Dispatch of rows that arrive already quantised (E4M3FN codes xq [T,H] with
+ * fp32 block scales xs [T,H/128]): no arithmetic, each token's codes and
+ * scales are copied to each of its receive rows. */
+void oracle_dispatch_fp8_input(const uint8_t* xq, const float* xs, int T, int H, int K,
+                               const int32_t* slot, uint8_t* recv, float* scales)
+{
+    int nb = H / 128;
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int32_t r = slot[(size_t)t * K + k];
+            if (r < 0)
+                continue;
+            memcpy(recv + (size_t)r * H, xq + (size_t)t * H, (size_t)H);
+            memcpy(scales + (size_t)r * nb, xs + (size_t)t * nb, sizeof(float) * (size_t)nb);
         }
     }
 }

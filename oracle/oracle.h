@@ -56,6 +56,10 @@ int oracle_layout(const int64_t* topk_idx, int T, int K, int E, int P,
 /* Exclusive prefix sum of per-expert counts: off[0] = 0, off[E] = N. */
 void oracle_expert_offsets(const int32_t* num_tokens_per_expert, int E, int32_t* off);
 
+/* GEMM-aligned offsets: off[e+1] = off[e] + (count rounded up to a multiple
+ * of A); rows [off[e] + count[e], off[e+1]) are padding. */
+void oracle_expert_offsets_aligned(const int32_t* num_tokens_per_expert, int E, int A, int32_t* off);
+
 /* Step 2, slots.  slot[T*K] (-1 when not dispatched), src_token[capacity]
  * (entries at and beyond min(N, capacity) are left untouched), *overflow = 1
  * when a pair's slot would be >= capacity. */
@@ -81,6 +85,11 @@ void oracle_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* slot
  * w[t,k] * y[slot[t,k], j], starting from +0.0f, skipping slot < 0 ). */
 void oracle_combine(const uint16_t* y, int T, int H, int K, const int32_t* slot,
                     const float* w, uint16_t* out);
+
+/* Dispatch of pre-quantised rows: recv[slot[t,k]] = xq[t] (H codes) and
+ * scales[slot[t,k]] = xs[t] (H/128 fp32). */
+void oracle_dispatch_fp8_input(const uint8_t* xq, const float* xs, int T, int H, int K,
+                               const int32_t* slot, uint8_t* recv, float* scales);
 
 /* Combine of FP8 rows q [rows, H] with fp32 block scales [rows, H/128]:
  *   v = e4m3fn_to_f32(q) * scale   (one fp32 multiply)

@@ -669,3 +669,71 @@ def test_combine_fp8_round_trip_within_fp8_error():
     s_tok = np.repeat(r["recv_scales"][np.maximum(r["slot"][:, 0], 0)], 128, axis=1)
     bound = kk * (2.0 ** -4 * np.abs(xf) + 2.0 ** -10 * s_tok) + 2.0 ** -8 * kk * np.abs(xf) + 1e-30
     assert np.all(np.abs(out - kk * xf) <= bound)
+
+
+# ----------------------------------------------------------------------------
+# GEMM-facing layouts: aligned expert blocks, pre-quantised FP8 input
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("A", [1, 4, 64, 128])
+def test_aligned_offsets_closed_form(A):
+    rng = np.random.default_rng(A)
+    cnt = rng.integers(0, 300, 97).astype(np.int32)
+    cnt[::7] = 0
+    off = oracle.expert_offsets(cnt, A)
+    block = -(-cnt.astype(np.int64) // A) * A          # smallest multiple of A >= count
+    assert off[0] == 0 and np.array_equal(np.diff(off), block)
+    assert np.all(off % A == 0)
+    if A == 1:
+        assert np.array_equal(off[1:], np.cumsum(cnt))
+
+
+@pytest.mark.parametrize("A,use_fp8", [(16, False), (128, True)])
+def test_aligned_dispatch_places_rows_and_zero_padding(A, use_fp8):
+    T, H, E, K = 300, 256, 24, 4
+    idx, w = workloads.random_case(55 + A, T, E, K, mask_frac=0.05)
+    x = workloads.random_rows(56, T, H, "wide" if use_fp8 else "normal")
+    r = oracle.run_all(idx, w, x, E, 4, use_fp8, align=A)
+    off, cnt = r["expert_offset"], r["num_tokens_per_expert"]
+    assert r["overflow"] == 0 and r["rows"] == off[-1] and r["N"] == cnt.sum()
+    # rows of expert e: [off[e], off[e] + cnt[e]), ascending source token
+    dense = oracle.run_all(idx, w, x, E, 4, use_fp8)
+    doff = dense["expert_offset"]
+    for t in range(T):
+        for k in range(K):
+            s, sd = r["slot"][t, k], dense["slot"][t, k]
+            assert (s < 0) == (sd < 0)
+            if s >= 0:
+                e = idx[t, k]
+                assert s - off[e] == sd - doff[e]            # same rank within the expert
+                assert np.array_equal(r["recv_x"][s], dense["recv_x"][sd])
+    pad = np.ones(r["rows"], bool)
+    for e in range(E):
+        pad[off[e]:off[e] + cnt[e]] = False
+    assert np.all(r["recv_x"][pad] == 0)
+    if use_fp8:
+        assert np.all(r["recv_scales"][pad] == 0)
+    assert np.all(r["src_token"][pad] == -1)
+
+
+def test_fp8_input_dispatch_copies_codes_and_scales():
+    T, H, E, K = 200, 512, 16, 4
+    idx, w = workloads.random_case(61, T, E, K, mask_frac=0.1)
+    rng = np.random.default_rng(62)
+    xq = rng.integers(0, 256, (T, H), dtype=np.uint32).astype(np.uint8)
+    xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+    r = oracle.run_all(idx, w, None, E, 4, True)
+    recv, sc = oracle.dispatch_fp8_input(xq, xs, r["slot"], r["rows"])
+    src = r["src_token"]
+    assert np.all(src >= 0)
+    assert np.array_equal(recv, xq[src]) and np.array_equal(sc.view(np.uint32), xs[src].view(np.uint32))
+    # passing dispatch's own per-token quantisation through reproduces the quantising dispatch
+    x = workloads.random_rows(63, T, H, "wide")
+    q = np.empty((T, H), np.uint8)
+    s = np.empty((T, H // 128), np.float32)
+    for t in range(T):
+        for b in range(H // 128):
+            q[t, b * 128:(b + 1) * 128], s[t, b] = oracle.quant_block(x[t, b * 128:(b + 1) * 128])
+    r2 = oracle.run_all(idx, w, x, E, 4, True)
+    recv2, sc2 = oracle.dispatch_fp8_input(q, s, r2["slot"], r2["rows"])
+    assert np.array_equal(recv2, r2["recv_x"]) and np.array_equal(sc2, r2["recv_scales"])
