@@ -66,6 +66,10 @@ class ep_handle_t(ctypes.Structure):
         ("chunk_pcnt", ctypes.c_void_p),
         ("chunk_inv", ctypes.c_void_p),
         ("chunk_cnt", ctypes.c_void_p),
+        ("expert_alignment", ctypes.c_int32),
+        ("scale_ld", ctypes.c_int32),
+        ("fp8_input", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -82,6 +86,10 @@ _SIGS = {
                                 ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_dispatch": ([_P, _P, _I, _I, _P, _P, _I, ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_dispatch_cached": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
+    "ep_get_dispatch_layout_aligned": ([_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                        ctypes.POINTER(ep_handle_t), _P], _I),
+    "ep_dispatch_ex": ([_P, _P, _P, _I, _I, _I, _P, _P, _I, ctypes.POINTER(ep_handle_t), _P], _I),
+    "ep_dispatch_cached_ex": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_combine_fp8": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_dispatch_backward_fp8": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P], _I),
     "ep_low_latency_dispatch": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
@@ -159,6 +167,28 @@ def ep_low_latency_dispatch(x, topk_idx, topk_weights, num_tokens, hidden, num_t
                                           num_tokens_per_partition, num_tokens_per_expert,
                                           is_token_in_partition, num_invalid, ws, ws_bytes,
                                           ctypes.byref(handle), stream)
+
+
+def ep_get_dispatch_layout_aligned(topk_idx, num_tokens, num_topk, num_experts, num_partitions,
+                                   expert_alignment, num_tokens_per_partition,
+                                   num_tokens_per_expert, is_token_in_partition, num_invalid, ws,
+                                   ws_bytes, handle, stream) -> int:
+    return load().ep_get_dispatch_layout_aligned(topk_idx, num_tokens, num_topk, num_experts,
+                                                 num_partitions, expert_alignment,
+                                                 num_tokens_per_partition, num_tokens_per_expert,
+                                                 is_token_in_partition, num_invalid, ws, ws_bytes,
+                                                 ctypes.byref(handle), stream)
+
+
+def ep_dispatch_ex(x, x_scales, topk_weights, hidden, use_fp8, scale_ld, recv_x, recv_scales,
+                   capacity_rows, handle, stream) -> int:
+    return load().ep_dispatch_ex(x, x_scales, topk_weights, hidden, int(use_fp8), scale_ld, recv_x,
+                                 recv_scales, capacity_rows, ctypes.byref(handle), stream)
+
+
+def ep_dispatch_cached_ex(x, x_scales, handle, recv_x, recv_scales, stream) -> int:
+    return load().ep_dispatch_cached_ex(x, x_scales, ctypes.byref(handle), recv_x, recv_scales,
+                                        stream)
 
 
 def ep_dispatch_cached(x, handle, recv_x, recv_scales, stream) -> int:
@@ -273,10 +303,12 @@ class Layout:
     handle: Handle
 
 
-def get_dispatch_layout(topk_idx, num_experts: int, num_partitions: int, ws=None) -> Layout:
+def get_dispatch_layout(topk_idx, num_experts: int, num_partitions: int, ws=None,
+                        expert_alignment: int = 1) -> Layout:
     """topk_idx: int64 [T, K] on the GPU.  Returns the counts, the mask and a
     handle for ``dispatch``.  ``ws`` (uint8, >= ep_workspace_bytes) may be
-    passed to reuse a workspace."""
+    passed to reuse a workspace.  expert_alignment > 1 rounds each expert's
+    block of receive rows up to a multiple of it (zeroed padding rows)."""
     import torch
     T, K = topk_idx.shape
     dev = topk_idx.device
@@ -290,31 +322,42 @@ def get_dispatch_layout(topk_idx, num_experts: int, num_partitions: int, ws=None
     itip = torch.empty((T, num_partitions), dtype=torch.uint8, device=dev)
     ninv = torch.empty(1, dtype=torch.int32, device=dev)
     h = ep_handle_t()
-    _check(ep_get_dispatch_layout(_ptr(topk_idx.contiguous()), T, K, num_experts, num_partitions,
-                                  _ptr(ntpp), _ptr(ntpe), _ptr(itip), _ptr(ninv), _ptr(ws),
-                                  ws.numel(), h, _stream()))
+    _check(ep_get_dispatch_layout_aligned(_ptr(topk_idx.contiguous()), T, K, num_experts,
+                                          num_partitions, int(expert_alignment), _ptr(ntpp),
+                                          _ptr(ntpe), _ptr(itip), _ptr(ninv), _ptr(ws), ws.numel(),
+                                          h, _stream()))
     return Layout(ntpp, ntpe, itip, ninv, Handle(h, ws))
 
 
-def dispatch(x, topk_weights, layout: Layout, use_fp8: bool, capacity_rows: Optional[int] = None):
-    """x: bf16 [T, H]; topk_weights: fp32 [T, K] or None.
+def dispatch(x, topk_weights, layout: Layout, use_fp8: bool, capacity_rows: Optional[int] = None,
+             x_scales=None, column_major_scales: bool = False):
+    """x: bf16 [T, H] (or, with x_scales fp32 [T, H/128], E4M3FN codes [T, H]
+    passed through unchanged); topk_weights: fp32 [T, K] or None.
     Returns (recv_x, recv_scales or None, handle).  recv_x is float8_e4m3fn
     [capacity, H] in FP8 mode, else bf16 [capacity, H]; capacity defaults to
-    T*K (no host sync)."""
+    the worst case T*K (+ E*(A-1) for an aligned layout), so no host sync.
+    column_major_scales stores recv_scales as [H/128, ld], ld = capacity
+    rounded up to a multiple of 4."""
     import torch
     h = layout.handle
     T, H = x.shape
     K = h.num_topk
-    cap = T * K if capacity_rows is None else int(capacity_rows)
+    A = max(1, h.c.expert_alignment)
+    cap = T * K + h.c.num_experts * (A - 1) if capacity_rows is None else int(capacity_rows)
     dev = x.device
+    scale_ld = 0
     if use_fp8:
         recv = torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev)
-        scales = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
+        if column_major_scales:
+            scale_ld = (cap + 3) // 4 * 4
+            scales = torch.empty((H // 128, scale_ld), dtype=torch.float32, device=dev)
+        else:
+            scales = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
     else:
         recv = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
         scales = None
-    _check(ep_dispatch(_ptr(x), _ptr(topk_weights), H, int(use_fp8), _ptr(recv), _ptr(scales),
-                       cap, h.c, _stream()))
+    _check(ep_dispatch_ex(_ptr(x), _ptr(x_scales), _ptr(topk_weights), H, int(use_fp8), scale_ld,
+                          _ptr(recv), _ptr(scales), cap, h.c, _stream()))
     return recv, scales, h
 
 
@@ -356,8 +399,9 @@ def low_latency_dispatch(x, topk_idx, topk_weights, num_experts: int, num_partit
     return recv, scales, lay
 
 
-def dispatch_cached(x, handle: Handle, recv_x=None, recv_scales=None):
-    """Re-send new rows along a dispatched handle's routing."""
+def dispatch_cached(x, handle: Handle, recv_x=None, recv_scales=None, x_scales=None):
+    """Re-send new rows along a dispatched handle's routing (same options:
+    x_scales exactly when the handle was dispatched from FP8 input)."""
     import torch
     c = handle.c
     cap, H = c.capacity_rows, c.hidden
@@ -365,8 +409,10 @@ def dispatch_cached(x, handle: Handle, recv_x=None, recv_scales=None):
         recv_x = torch.empty((cap, H), dtype=torch.float8_e4m3fn if c.use_fp8 else torch.bfloat16,
                              device=x.device)
     if c.use_fp8 and recv_scales is None:
-        recv_scales = torch.empty((cap, H // 128), dtype=torch.float32, device=x.device)
-    _check(ep_dispatch_cached(_ptr(x), c, _ptr(recv_x), _ptr(recv_scales), _stream()))
+        shape = (H // 128, c.scale_ld) if c.scale_ld else (cap, H // 128)
+        recv_scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check(ep_dispatch_cached_ex(_ptr(x), _ptr(x_scales), c, _ptr(recv_x), _ptr(recv_scales),
+                                 _stream()))
     return recv_x, recv_scales
 
 

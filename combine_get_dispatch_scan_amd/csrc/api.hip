@@ -95,7 +95,7 @@ int check_handle(const ep_handle_t* h, int min_stage)
 
 extern "C" {
 
-int ep_version(void) { return 10000; }
+int ep_version(void) { return 10100; }
 
 const char* ep_last_error(void) { return g_err.c_str(); }
 
@@ -112,10 +112,27 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
                            void* ws, size_t ws_bytes, ep_handle_t* handle,
                            hipStream_t stream)
 {
+    return ep_get_dispatch_layout_aligned(topk_idx, T, K, E, P, 1, num_tokens_per_partition,
+                                          num_tokens_per_expert, is_token_in_partition,
+                                          num_invalid, ws, ws_bytes, handle, stream);
+}
+
+int ep_get_dispatch_layout_aligned(const int64_t* topk_idx, int T, int K, int E, int P,
+                                   int expert_alignment, int32_t* num_tokens_per_partition,
+                                   int32_t* num_tokens_per_expert,
+                                   uint8_t* is_token_in_partition, int32_t* num_invalid,
+                                   void* ws, size_t ws_bytes, ep_handle_t* handle,
+                                   hipStream_t stream)
+{
     g_err.clear();
     int rc = check_dims(T, K, E, P);
     if (rc)
         return rc;
+    const int A = expert_alignment;
+    if (A < 1 || A > EP_MAX_ALIGNMENT)
+        return fail(EP_EINVAL, "expert_alignment=%d must be in [1, %d]", A, EP_MAX_ALIGNMENT);
+    if ((int64_t)T * K + (int64_t)E * (A - 1) >= ((int64_t)1 << 31))
+        return fail(EP_EINVAL, "T*K + E*(expert_alignment-1) must be < 2^31");
     if (!handle)
         return fail(EP_EINVAL, "handle is NULL");
     if (T > 0 && (!topk_idx || !aligned(topk_idx, 8)))
@@ -146,7 +163,8 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
     h.ws_bytes = ws_bytes;
     h.expert_offset = reinterpret_cast<int32_t*>(w + L.expert_offset);
     h.slot = reinterpret_cast<int32_t*>(w + L.slot);
-    h.src_token = reinterpret_cast<int32_t*>(w + L.src_token);
+    // the source-token table has T*K rows: kept for dense layouts only
+    h.src_token = A == 1 ? reinterpret_cast<int32_t*>(w + L.src_token) : nullptr;
     h.weights = reinterpret_cast<float*>(w + L.weights);
     h.status = reinterpret_cast<int32_t*>(w + L.status);
     h.pair_code = reinterpret_cast<int32_t*>(w + L.pair_code);
@@ -154,8 +172,9 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
     h.chunk_base = reinterpret_cast<int32_t*>(w + L.chunk_base);
     h.chunk_pcnt = reinterpret_cast<int32_t*>(w + L.chunk_pcnt);
     h.chunk_inv = reinterpret_cast<int32_t*>(w + L.chunk_inv);
+    h.expert_alignment = A;
 
-    hipError_t e = moe_ep::launch_layout(topk_idx, T, K, E, P, is_token_in_partition,
+    hipError_t e = moe_ep::launch_layout(topk_idx, T, K, E, P, A, is_token_in_partition,
                                          h.pair_code, h.chunk_cnt, h.chunk_base, h.chunk_pcnt,
                                          h.chunk_inv, h.expert_offset, num_tokens_per_expert,
                                          num_tokens_per_partition, num_invalid, h.status, stream);
@@ -163,6 +182,16 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
         return hip_fail(e, "layout launch");
     *handle = h;
     return EP_OK;
+}
+
+// Largest receive buffer a handle can need: T*K rows, plus E*(A-1) padding
+// rows for an aligned layout, or E*cap rows for a static one.
+static int64_t max_rows(const ep_handle_t* h)
+{
+    if (h->static_cap)
+        return (int64_t)h->num_experts * h->static_cap;
+    const int A = h->expert_alignment > 1 ? h->expert_alignment : 1;
+    return (int64_t)h->num_tokens * h->num_topk + (int64_t)h->num_experts * (A - 1);
 }
 
 static int check_rows(const ep_handle_t* h, const void* x, int H, int use_fp8, const void* recv_x,
@@ -175,11 +204,9 @@ static int check_rows(const ep_handle_t* h, const void* x, int H, int use_fp8, c
         return fail(EP_EINVAL, "use_fp8 must be 0 or 1");
     if (use_fp8 && H % 128 != 0)
         return fail(EP_EINVAL, "FP8 dispatch needs hidden %% 128 == 0 (hidden=%d)", H);
-    const int64_t max_rows = h->static_cap ? (int64_t)h->num_experts * h->static_cap
-                                           : (int64_t)T * h->num_topk;
-    if (capacity < 0 || (int64_t)capacity > max_rows)
-        return fail(EP_EINVAL, "capacity_rows=%d must be in [0, %lld]", capacity,
-                    (long long)max_rows);
+    const int64_t mr = max_rows(h);
+    if (capacity < 0 || (int64_t)capacity > mr)
+        return fail(EP_EINVAL, "capacity_rows=%d must be in [0, %lld]", capacity, (long long)mr);
     if (T > 0 && (!x || !aligned(x, 16)))
         return fail(EP_EINVAL, "x must be a non-NULL 16-byte aligned device pointer");
     if (capacity > 0 && (!recv_x || !aligned(recv_x, 16)))
@@ -189,11 +216,34 @@ static int check_rows(const ep_handle_t* h, const void* x, int H, int use_fp8, c
     return EP_OK;
 }
 
+// Options of ep_dispatch_ex: pre-quantised input and the scale layout.
+static int check_options(const ep_handle_t* h, const float* x_scales, int use_fp8, int scale_ld,
+                         int capacity)
+{
+    if (x_scales && !use_fp8)
+        return fail(EP_EINVAL, "x_scales (pre-quantised FP8 input) needs use_fp8 = 1");
+    if (x_scales && h->num_tokens > 0 && !aligned(x_scales, 4))
+        return fail(EP_EINVAL, "x_scales must be a 4-byte aligned device pointer");
+    if (scale_ld != 0) {
+        if (!use_fp8)
+            return fail(EP_EINVAL, "scale_ld (column-major scales) needs use_fp8 = 1");
+        if (scale_ld < capacity || scale_ld % 4 != 0)
+            return fail(EP_EINVAL, "scale_ld=%d must be 0, or >= capacity_rows=%d and a multiple of 4",
+                        scale_ld, capacity);
+    }
+    return EP_OK;
+}
+
 static int run_dispatch(const ep_handle_t* h, const void* x, const float* w_in, void* recv_x,
-                        float* recv_scales, bool fresh, hipStream_t stream)
+                        float* recv_scales, bool fresh, hipStream_t stream,
+                        const float* x_scales = nullptr)
 {
     moe_ep::DispatchLaunch L;
     L.x = x;
+    L.x_scales = x_scales;
+    L.align = h->expert_alignment > 1 ? h->expert_alignment : 1;
+    L.scale_ld = h->scale_ld;
+    L.chunk_cnt = h->chunk_cnt;
     L.T = h->num_tokens;
     L.H = h->hidden;
     L.K = h->num_topk;
@@ -221,6 +271,14 @@ int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp
                 void* recv_x, float* recv_scales, int capacity_rows,
                 ep_handle_t* handle, hipStream_t stream)
 {
+    return ep_dispatch_ex(x, nullptr, topk_weights, hidden, use_fp8, 0, recv_x, recv_scales,
+                          capacity_rows, handle, stream);
+}
+
+int ep_dispatch_ex(const void* x, const float* x_scales, const float* topk_weights, int hidden,
+                   int use_fp8, int scale_ld, void* recv_x, float* recv_scales, int capacity_rows,
+                   ep_handle_t* handle, hipStream_t stream)
+{
     g_err.clear();
     int rc = check_handle(handle, 1);
     if (rc)
@@ -230,6 +288,9 @@ int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp
     rc = check_rows(handle, x, hidden, use_fp8, recv_x, recv_scales, capacity_rows);
     if (rc)
         return rc;
+    rc = check_options(handle, x_scales, use_fp8, scale_ld, capacity_rows);
+    if (rc)
+        return rc;
     if (topk_weights && !aligned(topk_weights, 4))
         return fail(EP_EINVAL, "topk_weights must be 4-byte aligned");
     ep_handle_t h = *handle;
@@ -237,7 +298,9 @@ int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp
     h.use_fp8 = use_fp8;
     h.capacity_rows = capacity_rows;
     h.has_weights = topk_weights != nullptr;
-    rc = run_dispatch(&h, x, topk_weights, recv_x, recv_scales, true, stream);
+    h.scale_ld = scale_ld;
+    h.fp8_input = x_scales != nullptr;
+    rc = run_dispatch(&h, x, topk_weights, recv_x, recv_scales, true, stream, x_scales);
     if (rc)
         return rc;
     h.stage = 2;
@@ -341,6 +404,12 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
 int ep_dispatch_cached(const void* x, const ep_handle_t* handle, void* recv_x, float* recv_scales,
                        hipStream_t stream)
 {
+    return ep_dispatch_cached_ex(x, nullptr, handle, recv_x, recv_scales, stream);
+}
+
+int ep_dispatch_cached_ex(const void* x, const float* x_scales, const ep_handle_t* handle,
+                          void* recv_x, float* recv_scales, hipStream_t stream)
+{
     g_err.clear();
     int rc = check_handle(handle, 2);
     if (rc)
@@ -349,7 +418,14 @@ int ep_dispatch_cached(const void* x, const ep_handle_t* handle, void* recv_x, f
                     handle->capacity_rows);
     if (rc)
         return rc;
-    return run_dispatch(handle, x, nullptr, recv_x, recv_scales, false, stream);
+    if (handle->fp8_input && !x_scales && handle->num_tokens > 0)
+        return fail(EP_EINVAL, "the handle was dispatched from FP8 input: pass x_scales");
+    if (!handle->fp8_input && x_scales)
+        return fail(EP_EINVAL, "the handle was dispatched from BF16 input: x_scales must be NULL");
+    rc = check_options(handle, x_scales, handle->use_fp8, handle->scale_ld, handle->capacity_rows);
+    if (rc)
+        return rc;
+    return run_dispatch(handle, x, nullptr, recv_x, recv_scales, false, stream, x_scales);
 }
 
 int ep_combine(const void* y, const ep_handle_t* handle, const float* topk_weights, void* out,

@@ -9,7 +9,12 @@
 // the pair codes left by the layout step into receive rows
 //     slot = expert_offset[e] + chunk_base[chunk][e] + rank_in_chunk
 // and broadcast them to the wave (readlane -> SGPRs); the row itself is then
-// handled by fp8_rows / bf16_rows (dispatch_rows.h).
+// handled by fp8_rows / fp8in_rows / bf16_rows (dispatch_rows.h).
+//
+// GEMM-facing options (GeekNews, "Những thay đổi chính của bản phát hành
+// V2": a new GEMM layout; usage section: counts per expert feed the grouped
+// GEMM): expert blocks aligned to a row tile with zeroed padding rows,
+// column-major block scales, and input that arrives already quantised.
 #include "device.h"
 #include "dispatch_rows.h"
 #include "launch.h"
@@ -18,11 +23,16 @@ namespace moe_ep {
 
 struct DispatchArgs {
     const uint16_t* x;
-    int T, H, K, E;
+    const float* x_scales;    // pre-quantised input: x holds E4M3FN codes
+    int T, H, K, E, B;
     int nseg, iters_per_seg, iters;
+    int row_blocks;           // workgroups that move rows; the rest zero padding
+    int align;                // rows per GEMM tile of an aligned layout (1: dense)
+    int scale_ld;             // 0: row-major scales, else column-major leading dim
     int capacity;
     const int32_t* pair_code;
     const int32_t* chunk_base;
+    const int32_t* chunk_cnt;
     const int32_t* expert_offset;
     const float* w_in;
     float* w_copy;
@@ -53,7 +63,7 @@ __device__ __forceinline__ int pair_slot(const DispatchArgs& a, int t, int seg)
             }
             if (seg == 0) {
                 a.slot[i] = s;
-                if (s >= 0)
+                if (s >= 0 && a.src_token)
                     a.src_token[s] = t;
                 if (a.w_in)
                     a.w_copy[i] = a.w_in[i];
@@ -67,38 +77,88 @@ __device__ __forceinline__ int pair_slot(const DispatchArgs& a, int t, int seg)
     return s;
 }
 
+// Workgroups past row_blocks zero the padding rows of a GEMM-aligned layout:
+// one wave per (expert, padding row index < align - 1).  Expert e's block is
+// [expert_offset[e], expert_offset[e+1]) and its rows from expert_offset[e] +
+// count(e) on are padding; count(e) is the last chunk's base plus its count.
+__device__ __forceinline__ void pad_item(const DispatchArgs& a, bool fp8)
+{
+    const int item = (blockIdx.x - a.row_blocks) * kDispatchWaves + threadIdx.x / kWave;
+    const int per = a.align - 1;
+    const int e = item / per;
+    if (e >= a.E)
+        return;
+    const size_t last = (size_t)(a.B - 1) * a.E + e;
+    const int cnt = a.chunk_base[last] + a.chunk_cnt[last];
+    const int row = a.expert_offset[e] + cnt + item % per;
+    if (row >= a.expert_offset[e + 1] || row >= a.capacity)
+        return;
+    zero_row(a.recv, a.scales, row, a.H, fp8, a.scale_ld);
+}
+
+template <int KMAX>
+__device__ __forceinline__ void row_slots(const DispatchArgs& a, int s_own, int (&sk)[KMAX])
+{
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+}
+
 template <int KMAX, bool FRESH>
 __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(DispatchArgs a)
 {
+    if ((int)blockIdx.x >= a.row_blocks) {
+        pad_item(a, true);
+        return;
+    }
     const int wi = blockIdx.x * kDispatchWaves + threadIdx.x / kWave;
     const int t = wi / a.nseg;
     const int seg = wi % a.nseg;
     if (t >= a.T)
         return;
-    const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
     int sk[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+    row_slots<KMAX>(a, pair_slot<KMAX, FRESH>(a, t, seg), sk);
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
-    fp8_rows<KMAX>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end,
+    fp8_rows<KMAX>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end, a.scale_ld,
                    static_cast<uint8_t*>(a.recv), a.scales);
+}
+
+template <int KMAX, bool FRESH>
+__global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8in_kernel(DispatchArgs a)
+{
+    if ((int)blockIdx.x >= a.row_blocks) {
+        pad_item(a, true);
+        return;
+    }
+    const int wi = blockIdx.x * kDispatchWaves + threadIdx.x / kWave;
+    const int t = wi / a.nseg;
+    const int seg = wi % a.nseg;
+    if (t >= a.T)
+        return;
+    int sk[KMAX];
+    row_slots<KMAX>(a, pair_slot<KMAX, FRESH>(a, t, seg), sk);
+    const int i_begin = seg * a.iters_per_seg;
+    const int i_end = min(a.iters, i_begin + a.iters_per_seg);
+    fp8in_rows<KMAX>(reinterpret_cast<const uint8_t*>(a.x) + (size_t)t * a.H,
+                     a.x_scales + (size_t)t * (a.H / kQBlock), sk, a.H, i_begin, i_end, a.scale_ld,
+                     static_cast<uint8_t*>(a.recv), a.scales);
 }
 
 template <int KMAX, bool FRESH>
 __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_bf16_kernel(DispatchArgs a)
 {
+    if ((int)blockIdx.x >= a.row_blocks) {
+        pad_item(a, false);
+        return;
+    }
     const int wi = blockIdx.x * kDispatchWaves + threadIdx.x / kWave;
     const int t = wi / a.nseg;
     const int seg = wi % a.nseg;
     if (t >= a.T)
         return;
-    const int s_own = pair_slot<KMAX, FRESH>(a, t, seg);
     int sk[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+    row_slots<KMAX>(a, pair_slot<KMAX, FRESH>(a, t, seg), sk);
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
     bf16_rows<KMAX>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end,
@@ -111,13 +171,18 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
         return hipSuccess;
     DispatchArgs a;
     a.x = static_cast<const uint16_t*>(L.x);
+    a.x_scales = L.x_scales;
     a.T = L.T;
     a.H = L.H;
     a.K = L.K;
     a.E = L.E;
+    a.B = (L.T + kChunk - 1) / kChunk;
+    a.align = L.align;
+    a.scale_ld = L.scale_ld;
     a.capacity = L.capacity;
     a.pair_code = L.pair_code;
     a.chunk_base = L.chunk_base;
+    a.chunk_cnt = L.chunk_cnt;
     a.expert_offset = L.expert_offset;
     a.w_in = L.w_in;
     a.w_copy = L.w_copy;
@@ -134,7 +199,10 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
     a.nseg = rs.nseg;
     a.iters_per_seg = rs.iters_per_seg;
     const long long items = (long long)L.T * a.nseg;
-    dim3 grid((unsigned)((items + kDispatchWaves - 1) / kDispatchWaves));
+    a.row_blocks = (int)((items + kDispatchWaves - 1) / kDispatchWaves);
+    const long long pad_items = L.align > 1 ? (long long)L.E * (L.align - 1) : 0;
+    const long long pad_blocks = (pad_items + kDispatchWaves - 1) / kDispatchWaves;
+    dim3 grid((unsigned)(a.row_blocks + pad_blocks));
     dim3 block(kDispatchWaves * kWave);
 
 #define EP_DISPATCH(KERNEL, KM, FRESH) \
@@ -147,7 +215,10 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
         else EP_DISPATCH(KERNEL, 16, FRESH);          \
     } while (0)
 
-    if (L.use_fp8) {
+    if (L.use_fp8 && L.x_scales) {
+        if (L.fresh) EP_DISPATCH_K(dispatch_fp8in_kernel, true);
+        else EP_DISPATCH_K(dispatch_fp8in_kernel, false);
+    } else if (L.use_fp8) {
         if (L.fresh) EP_DISPATCH_K(dispatch_fp8_kernel, true);
         else EP_DISPATCH_K(dispatch_fp8_kernel, false);
     } else {

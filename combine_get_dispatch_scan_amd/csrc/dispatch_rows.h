@@ -41,13 +41,21 @@ constexpr int kBf16ChPerIter = kWave * 8;           // 512 channels per wave ste
 constexpr int kDispatchUnroll = EP_DISPATCH_UNROLL; // wave steps with loads in flight
 
 
+// Address of receive row r's scale of block b: row-major [rows][H/128] when
+// scale_ld == 0, else column-major [H/128][scale_ld] (each block's scales
+// contiguous over rows, the layout a grouped GEMM reads them in).
+__device__ __forceinline__ size_t scale_index(int r, int b, int nb, int scale_ld)
+{
+    return scale_ld ? (size_t)b * scale_ld + r : (size_t)r * nb + b;
+}
+
 // Quantise one wave step (lane: 16 channels from cb, in lo / hi) and store the
 // codes and block scales to the receive rows sk[].  Called by the whole wave:
 // lanes past the row end (active false) hold zeros and only join the amax
 // reduction.
 template <int KMAX>
 __device__ __forceinline__ void fp8_step_store(const u32x4& lo, const u32x4& hi, int cb, bool active,
-                                               const int (&sk)[KMAX], int H,
+                                               const int (&sk)[KMAX], int H, int scale_ld,
                                                uint8_t* __restrict__ recv, float* __restrict__ scales)
 {
     const int lane = lane_id();
@@ -84,7 +92,7 @@ __device__ __forceinline__ void fp8_step_store(const u32x4& lo, const u32x4& hi,
             if (sk[k] >= 0) {
                 store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, q);
                 if ((lane & 7) == 0)
-                    scales[(size_t)sk[k] * nb + blk] = scale;
+                    scales[scale_index(sk[k], blk, nb, scale_ld)] = scale;
             }
         }
     }
@@ -108,7 +116,7 @@ __device__ __forceinline__ bool fp8_step_load(const uint16_t* __restrict__ xrow,
 // x[t] row -> K receive rows over wave steps [i_begin, i_end) of 1024 channels
 template <int KMAX>
 __device__ __forceinline__ void fp8_rows(const uint16_t* __restrict__ xrow, const int (&sk)[KMAX],
-                                         int H, int i_begin, int i_end,
+                                         int H, int i_begin, int i_end, int scale_ld,
                                          uint8_t* __restrict__ recv, float* __restrict__ scales)
 {
     const int lane = lane_id();
@@ -130,7 +138,7 @@ __device__ __forceinline__ void fp8_rows(const uint16_t* __restrict__ xrow, cons
             if (i0 + u >= i_end)
                 break;
             fp8_step_store<KMAX>(lo[u], hi[u], (i0 + u) * kFp8ChPerIter + lane * 16, act[u], sk, H,
-                                 recv, scales);
+                                 scale_ld, recv, scales);
         }
     }
 }
@@ -167,6 +175,63 @@ __device__ __forceinline__ void bf16_rows(const uint16_t* __restrict__ xrow, con
             if (i0 + u < i_end && cb < H)
                 bf16_step_store<KMAX>(d[u], cb, sk, H, recv);
         }
+    }
+}
+
+// Pre-quantised input: the token's E4M3FN codes (16 per lane, 1024 channels
+// per wave step) and its block scales are copied to the receive rows sk[].
+template <int KMAX>
+__device__ __forceinline__ void fp8in_rows(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                                           const int (&sk)[KMAX], int H, int i_begin, int i_end,
+                                           int scale_ld, uint8_t* __restrict__ recv,
+                                           float* __restrict__ scales)
+{
+    const int lane = lane_id();
+    const int nb = H / kQBlock;
+    for (int i0 = i_begin; i0 < i_end; i0 += kDispatchUnroll) {
+        u32x4 d[kDispatchUnroll];
+        float sc[kDispatchUnroll];
+#pragma unroll
+        for (int u = 0; u < kDispatchUnroll; ++u) {
+            const int cb = (i0 + u) * kFp8ChPerIter + lane * 16;
+            if (i0 + u < i_end && cb < H) {
+                d[u] = load16_hint<EP_DISPATCH_NT_LOAD>(xq + cb);
+                sc[u] = xs[cb / kQBlock];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kDispatchUnroll; ++u) {
+            const int cb = (i0 + u) * kFp8ChPerIter + lane * 16;
+            if (i0 + u < i_end && cb < H) {
+                const int blk = cb / kQBlock;
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) {
+                    if (sk[k] >= 0) {
+                        store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, d[u]);
+                        if ((lane & 7) == 0)
+                            scales[scale_index(sk[k], blk, nb, scale_ld)] = sc[u];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Zero one padding row of a GEMM-aligned layout (its codes or BF16 values,
+// and its scales in FP8 mode).  Called by a whole wave.
+__device__ __forceinline__ void zero_row(void* __restrict__ recv, float* __restrict__ scales, int row,
+                                         int H, bool fp8, int scale_ld)
+{
+    const int lane = lane_id();
+    const size_t row_bytes = (size_t)H * (fp8 ? 1 : 2);
+    uint8_t* dst = static_cast<uint8_t*>(recv) + (size_t)row * row_bytes;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    for (size_t off = (size_t)lane * 16; off < row_bytes; off += kWave * 16)
+        store16_hint<EP_DISPATCH_NT_STORE>(dst + off, z);
+    if (fp8) {
+        const int nb = H / kQBlock;
+        for (int b = lane; b < nb; b += kWave)
+            scales[scale_index(row, b, nb, scale_ld)] = 0.0f;
     }
 }
 

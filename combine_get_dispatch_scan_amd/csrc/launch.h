@@ -7,7 +7,7 @@
 namespace moe_ep {
 
 // get_dispatch_layout: per-chunk count kernel + one-workgroup scan kernel.
-hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
+hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, int align,
                          uint8_t* is_token_in_partition, int32_t* pair_code,
                          int32_t* chunk_cnt, int32_t* chunk_base, int32_t* chunk_pcnt,
                          int32_t* chunk_inv, int32_t* expert_offset,
@@ -16,12 +16,16 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
 
 struct DispatchLaunch {
     const void* x;
+    const float* x_scales;    // non-null: x holds E4M3FN codes with these block scales
     int T, H, K, E;
     int use_fp8;
     bool fresh;               // compute slots from pair codes (else reuse slot[])
     int capacity;
+    int align;                // GEMM row tile of the expert blocks (1: dense)
+    int scale_ld;             // 0: row-major scales, else column-major leading dimension
     const int32_t* pair_code;
     const int32_t* chunk_base;
+    const int32_t* chunk_cnt;
     const int32_t* expert_offset;
     const float* w_in;
     float* w_copy;

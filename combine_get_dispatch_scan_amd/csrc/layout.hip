@@ -229,7 +229,7 @@ constexpr int kScanLdsInts = 16384;
 // loads, scanned in LDS and chunk_base is written out; larger tables are
 // scanned from global memory.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
-    int B, int E, int P,
+    int B, int E, int P, int align,
     const int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_base,
     const int32_t* __restrict__ chunk_pcnt, const int32_t* __restrict__ chunk_inv,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ num_tokens_per_expert,
@@ -276,10 +276,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
         itot = lds_tot[0];
     }
 
+    // an expert's block of receive rows: its count, rounded up to a multiple
+    // of align for GEMM-aligned layouts (the rest of the block is padding)
+    const int blk = align == 1 ? cnt : (cnt + align - 1) / align * align;
     int total = 0;
-    int incl = block_inclusive_scan<kScanThreads>(cnt, lds_wave, &total);
+    int incl = block_inclusive_scan<kScanThreads>(blk, lds_wave, &total);
     if (tid < E) {
-        expert_offset[tid] = incl - cnt;
+        expert_offset[tid] = incl - blk;
         num_tokens_per_expert[tid] = cnt;
     }
     if (tid < P)
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     }
 }
 
-hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
+hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, int align,
                          uint8_t* is_token_in_partition, int32_t* pair_code,
                          int32_t* chunk_cnt, int32_t* chunk_base, int32_t* chunk_pcnt,
                          int32_t* chunk_inv, int32_t* expert_offset,
@@ -322,7 +325,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P,
     }
     const bool staged = (long long)B * (E + P + 1) <= kScanLdsInts;
     const size_t scan_lds = staged ? (size_t)B * (E + P + 1) * sizeof(int) : 0;
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), scan_lds, stream, B, E, P,
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), scan_lds, stream, B, E, P, align,
                        chunk_cnt, chunk_base, chunk_pcnt, chunk_inv, expert_offset,
                        num_tokens_per_expert, num_tokens_per_partition, num_invalid, status);
     return hipGetLastError();

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kLLThreads) void low_latency_dispatch_kernel(LLArgs
     for (int k = 0; k < KMAX; ++k)
         sk[k] = k < K ? readlane(s_own, k) : -1;
     if (FP8)
-        fp8_step_store<KMAX>(lo, hi, cb, act, sk, a.H, static_cast<uint8_t*>(a.recv), a.scales);
+        fp8_step_store<KMAX>(lo, hi, cb, act, sk, a.H, 0, static_cast<uint8_t*>(a.recv), a.scales);
     else if (act)
         bf16_step_store<KMAX>(lo, cb, sk, a.H, static_cast<uint16_t*>(a.recv));
 }

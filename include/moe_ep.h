@@ -61,6 +61,7 @@ extern "C" {
 #define EP_MAX_HIDDEN      32768
 
 #define EP_MAX_LL_TOKENS   256     /* tokens per ep_low_latency_dispatch call     */
+#define EP_MAX_ALIGNMENT   1024    /* expert_alignment of an aligned layout        */
 
 #define EP_HANDLE_MAGIC    0x31485045u   /* "EPH1" */
 
@@ -98,6 +99,11 @@ typedef struct ep_handle {
     int32_t* chunk_pcnt;       /* [chunks*P] */
     int32_t* chunk_inv;        /* [chunks]   */
     int32_t* chunk_cnt;        /* [chunks*E] rows of expert e in each chunk        */
+    int32_t  expert_alignment; /* row tile of the expert blocks (1 or 0: dense)    */
+    int32_t  scale_ld;         /* 0: row-major scales; else column-major, this
+                                  leading dimension (set by ep_dispatch_ex)      */
+    int32_t  fp8_input;        /* 1 when ep_dispatch_ex got pre-quantised input    */
+    int32_t  reserved;
 } ep_handle_t;
 
 /* Library version, major*10000 + minor*100 + patch. */
@@ -198,6 +204,45 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
                             int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
                             uint8_t* is_token_in_partition, int32_t* num_invalid,
                             void* ws, size_t ws_bytes, ep_handle_t* handle, hipStream_t stream);
+
+/*
+ * GEMM-facing layout options (GeekNews, "Những thay đổi chính của bản phát
+ * hành V2": a new GEMM layout; usage section: per-expert counts feed the
+ * grouped GEMM; aikraft.ru "Технические детали и требования": FP8 input).
+ *
+ * ep_get_dispatch_layout_aligned: as ep_get_dispatch_layout, with each
+ * expert's block of receive rows rounded up to a multiple of
+ * expert_alignment (1 <= A <= EP_MAX_ALIGNMENT), so every block starts on a
+ * multiple of A.  Rows [off[e] + count[e], off[e+1]) of a block are padding,
+ * written as zero codes / zero BF16 values and zero scales by every dispatch
+ * through the handle.  The counts ep_handle_recv_counts reports are the block
+ * sizes (padding included); num_tokens_per_expert keeps the real counts.  The
+ * handle keeps no source-token table (src_token NULL) when A > 1.  A dispatch
+ * without drops needs capacity_rows >= T*K + E*(A-1) in the worst case.
+ *
+ * ep_dispatch_ex: ep_dispatch with two more options.
+ *   x_scales  NULL: x is BF16 as for ep_dispatch.  Non-NULL (needs use_fp8):
+ *             x holds E4M3FN codes [T*H] and x_scales fp32 [T*H/128] their
+ *             block scales; codes and scales are copied, not re-quantised.
+ *   scale_ld  0: recv_scales row-major [capacity_rows][H/128].  Otherwise
+ *             (FP8 only; >= capacity_rows, a multiple of 4) column-major:
+ *             the scale of receive row r, block b is recv_scales[b*scale_ld + r].
+ * ep_dispatch_cached_ex: the cached dispatch of such a handle; x_scales must
+ * be given exactly when the handle was dispatched from FP8 input.
+ * Errors: EP_EINVAL, EP_EHIP.
+ */
+int ep_get_dispatch_layout_aligned(const int64_t* topk_idx, int num_tokens, int num_topk,
+                                   int num_experts, int num_partitions, int expert_alignment,
+                                   int32_t* num_tokens_per_partition,
+                                   int32_t* num_tokens_per_expert,
+                                   uint8_t* is_token_in_partition, int32_t* num_invalid,
+                                   void* ws, size_t ws_bytes, ep_handle_t* handle,
+                                   hipStream_t stream);
+int ep_dispatch_ex(const void* x, const float* x_scales, const float* topk_weights, int hidden,
+                   int use_fp8, int scale_ld, void* recv_x, float* recv_scales, int capacity_rows,
+                   ep_handle_t* handle, hipStream_t stream);
+int ep_dispatch_cached_ex(const void* x, const float* x_scales, const ep_handle_t* handle,
+                          void* recv_x, float* recv_scales, hipStream_t stream);
 
 /*
  * Cached dispatch: re-sends new token rows along the routing of an earlier
