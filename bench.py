@@ -372,7 +372,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dom_ms = mean([e[0].elapsed_time(e[1]) for e in dev_ev])
+    dom_all = sorted(e[0].elapsed_time(e[1]) for e in dev_ev)
+    dom_ms = mean(dom_all)
+    dom_stats = {"median": round(dom_all[len(dom_all) // 2] * 1e3, 2), "min": round(dom_all[0] * 1e3, 2),
+                 "p90": round(dom_all[min(len(dom_all) - 1, int(0.9 * len(dom_all)))] * 1e3, 2)}
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {dom} {dom_ms * 1e3:.2f} us",
           file=sys.stderr, flush=True)
 
@@ -501,6 +504,7 @@ def main():
             "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
+            "launch_us": dom_stats,
             "traffic": measured_traffic(args.config, dom_kernel),
         },
         "phases_us": {k: round(v * 1e3, 2) for k, v in phases.items()},

@@ -20,10 +20,10 @@ namespace moe_ep {
 #define EP_COMBINE_UNROLL 2
 #endif
 #ifndef EP_COMBINE_MIN_ITEMS
-#define EP_COMBINE_MIN_ITEMS 65536
+#define EP_COMBINE_MIN_ITEMS 131072
 #endif
 #ifndef EP_COMBINE_MAX_ITERS
-#define EP_COMBINE_MAX_ITERS 4
+#define EP_COMBINE_MAX_ITERS 2
 #endif
 #ifndef EP_COMBINE_WAVES
 #define EP_COMBINE_WAVES 4
