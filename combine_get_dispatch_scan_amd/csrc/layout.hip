@@ -220,6 +220,67 @@ __device__ __forceinline__ void column_scan(const In* m, Out* out, int B, int W,
     __syncthreads();
 }
 
+// A batch of at most 256 tokens is one chunk: its counts are already the
+// totals, so the workgroup that counts also scans (each thread owns up to 4
+// consecutive experts) and the scan kernel's launch is saved.
+template <int KMAX>
+__global__ __launch_bounds__(kChunk) void layout_single_kernel(
+    const int64_t* __restrict__ topk_idx, int T, int K, int E, int P, int align,
+    uint8_t* __restrict__ is_token_in_partition, bool wide_mask_store,
+    int32_t* __restrict__ pair_code, int32_t* __restrict__ chunk_cnt,
+    int32_t* __restrict__ chunk_base, int32_t* __restrict__ chunk_pcnt,
+    int32_t* __restrict__ chunk_inv, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_tokens_per_partition,
+    int32_t* __restrict__ num_invalid, int32_t* __restrict__ status)
+{
+    extern __shared__ unsigned long long lds_bits[];     // [E][kChunkWaves]
+    __shared__ int lds_pcnt[64];
+    __shared__ int lds_inv;
+    __shared__ int lds_wave[kChunk / kWave];
+    count_chunk<KMAX>(topk_idx, T, K, E, P, 0, is_token_in_partition, wide_mask_store,
+                      pair_code, chunk_cnt, chunk_pcnt, chunk_inv, lds_bits, lds_pcnt, &lds_inv);
+    // the masks and partition / invalid counts in LDS are final here
+    const int tid = threadIdx.x;
+    const int epT = (E + kChunk - 1) / kChunk;            // <= 4 (E <= 1024)
+    int n_e[4], blk_e[4];
+    int part = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid * epT + j;
+        n_e[j] = 0;
+        blk_e[j] = 0;
+        if (j < epT && e < E) {
+#pragma unroll
+            for (int w = 0; w < kChunkWaves; ++w)
+                n_e[j] += __popcll(lds_bits[e * kChunkWaves + w]);
+            blk_e[j] = align == 1 ? n_e[j] : (n_e[j] + align - 1) / align * align;
+            part += blk_e[j];
+        }
+    }
+    int total = 0;
+    int run = block_inclusive_scan<kChunk>(part, lds_wave, &total) - part;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid * epT + j;
+        if (j < epT && e < E) {
+            expert_offset[e] = run;
+            num_tokens_per_expert[e] = n_e[j];
+            chunk_base[e] = 0;
+            run += blk_e[j];
+        }
+    }
+    if (tid < P)
+        num_tokens_per_partition[tid] = lds_pcnt[tid];
+    if (tid == 0) {
+        expert_offset[E] = total;
+        num_invalid[0] = lds_inv;
+        status[0] = 0;
+        status[1] = lds_inv;
+        status[2] = total;
+        status[3] = 0;
+    }
+}
+
 // Largest per-chunk table set (B * (E + P + 1) ints) staged through LDS.
 constexpr int kScanLdsInts = 16384;
 
@@ -308,6 +369,20 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, in
     const size_t lds = (size_t)E * kChunkWaves * sizeof(unsigned long long);
     // 8 partition bytes per 64-bit store when rows start 8-byte aligned
     const bool wide = (P % 8 == 0) && ((reinterpret_cast<uintptr_t>(is_token_in_partition) & 7) == 0);
+    if (B == 1) {
+        dim3 grid(1), block(kChunk);
+#define EP_LAYOUT1(KM)                                                                         \
+        hipLaunchKernelGGL(layout_single_kernel<KM>, grid, block, lds, stream, topk_idx, T, K, \
+                           E, P, align, is_token_in_partition, wide, pair_code, chunk_cnt,     \
+                           chunk_base, chunk_pcnt, chunk_inv, expert_offset,                   \
+                           num_tokens_per_expert, num_tokens_per_partition, num_invalid, status)
+        if (K <= 2) EP_LAYOUT1(2);
+        else if (K <= 4) EP_LAYOUT1(4);
+        else if (K <= 8) EP_LAYOUT1(8);
+        else EP_LAYOUT1(16);
+#undef EP_LAYOUT1
+        return hipGetLastError();
+    }
     if (B > 0) {
         dim3 grid(B), block(kChunk);
 #define EP_LAYOUT(KM)                                                                   \
