@@ -737,3 +737,143 @@ def test_fp8_input_dispatch_copies_codes_and_scales():
     r2 = oracle.run_all(idx, w, x, E, 4, True)
     recv2, sc2 = oracle.dispatch_fp8_input(q, s, r2["slot"], r2["rows"])
     assert np.array_equal(recv2, r2["recv_x"]) and np.array_equal(sc2, r2["recv_scales"])
+
+
+# ----------------------------------------------------------------------------
+# the oracle's own memory safety: every entry point under ASan + UBSan
+# ----------------------------------------------------------------------------
+
+def test_oracle_under_address_and_undefined_sanitizers(tmp_path):
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "oracle_sanitize"
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-ffp-contract=off", "-I", os.path.join(root, "oracle"),
+           os.path.join(root, "tests", "oracle_sanitize_driver.c"),
+           os.path.join(root, "oracle", "oracle.c"), "-lm", "-o", str(exe)]
+    built = subprocess.run(cmd, capture_output=True, text=True)
+    if built.returncode != 0 and "sanitize" in built.stderr:
+        pytest.skip("sanitizer runtime not available: " + built.stderr[-200:])
+    assert built.returncode == 0, built.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert run.returncode == 0, run.stderr[-3000:]
+    assert "oracle sanitizer run: ok" in run.stdout
+
+
+# ----------------------------------------------------------------------------
+# brute force on tiny cases: an independent pure-Python reading of the steps
+# ----------------------------------------------------------------------------
+
+def _brute_layout_slots(idx, E, P, cap):
+    """Layout and slots enumerated the slow way: rows of expert 0 first, in
+    token order, then expert 1, ..."""
+    T, K = idx.shape
+    epp = E // P
+    valid = np.zeros((T, K), np.uint8)
+    cnt = [0] * E
+    mask = np.zeros((T, P), np.uint8)
+    ninv = 0
+    for t in range(T):
+        seen = set()
+        for k in range(K):
+            e = int(idx[t, k])
+            if e < 0:
+                continue
+            if e >= E or e in seen:
+                ninv += 1
+                continue
+            seen.add(e)
+            valid[t, k] = 1
+            cnt[e] += 1
+            mask[t, e // epp] = 1
+    order = [(t, k) for e in range(E) for t in range(T) for k in range(K)
+             if valid[t, k] and int(idx[t, k]) == e]
+    slot = np.full((T, K), -1, np.int32)
+    ovf = 0
+    for r, (t, k) in enumerate(order):
+        if r < cap:
+            slot[t, k] = r
+        else:
+            ovf = 1
+    return dict(num_tokens_per_expert=np.array(cnt, np.int32), is_token_in_partition=mask,
+                num_tokens_per_partition=mask.sum(axis=0).astype(np.int32), num_invalid=ninv,
+                slot=slot, overflow=ovf)
+
+
+def _rn_f32(q):
+    """Round an exact rational to the nearest fp32, ties to even."""
+    from fractions import Fraction
+    if q == 0:
+        return 0.0
+    s = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                        # below the normal range: quantum 2^-149
+    m = a / Fraction(2) ** (e - 23)
+    n = int(m)
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return s * float(np.float32(n * 2.0 ** (e - 23)))
+
+
+def test_brute_force_tiny_cases_1000_seeds():
+    rng = np.random.default_rng(2024)
+    for seed in range(1000):
+        T, E, K = int(rng.integers(0, 9)), int(rng.choice([1, 2, 4, 8])), int(rng.integers(1, 4))
+        P = int(rng.choice([p for p in (1, 2, 4) if E % p == 0]))
+        idx = rng.integers(-2, E + 2, (T, K)).astype(np.int64)
+        cap = int(rng.integers(0, T * K + 1)) if seed % 3 == 0 else T * K
+        ref = _brute_layout_slots(idx, E, P, cap)
+        r = oracle.run_all(idx, np.ones((T, K), np.float32), None, E, P, False, capacity=cap)
+        for key in ("num_tokens_per_expert", "num_tokens_per_partition", "is_token_in_partition",
+                    "slot"):
+            assert np.array_equal(r[key], ref[key]), (seed, key)
+        assert r["num_invalid"] == ref["num_invalid"] and r["overflow"] == ref["overflow"], seed
+
+
+def test_brute_force_tiny_dispatch_and_combine():
+    """FP8 quantisation by nearest-value search and combine by exact rational
+    arithmetic with one rounding per fma, on 200 tiny random cases."""
+    from fractions import Fraction
+    rng = np.random.default_rng(77)
+    H = 128
+    for seed in range(200):
+        T, E, K = int(rng.integers(1, 9)), int(rng.choice([2, 4, 8])), int(rng.integers(1, 4))
+        idx = rng.integers(-1, E, (T, K)).astype(np.int64)
+        w = rng.random((T, K)).astype(np.float32)
+        x = workloads.random_rows(seed, T, H, ["normal", "wide", "bits", "subnormal"][seed % 4])
+        r = oracle.run_all(idx, w, x, E, 1, True)
+        ref = _brute_layout_slots(idx, E, 1, T * K)
+        assert np.array_equal(r["slot"], ref["slot"])
+        xf = _f32(x)
+        for t in range(T):
+            a = np.float32(max(np.float32(np.abs(xf[t]).max()), np.float32(2.0 ** -64)))
+            inv = np.float32(448.0) / a
+            s = a / np.float32(448.0)
+            v = (xf[t] * inv).astype(np.float32)
+            codes = _nearest_brute(v)
+            for k in range(K):
+                if ref["slot"][t, k] >= 0:
+                    assert np.array_equal(r["recv_x"][ref["slot"][t, k]], codes), (seed, t, k)
+                    assert r["recv_scales"][ref["slot"][t, k], 0] == s
+        # combine of random BF16 rows with exact fma emulation
+        y = workloads.random_rows(seed + 5000, max(r["rows"], 1), H)
+        yf = _f32(y)
+        out = _f32(oracle.combine(y, r["slot"], w))
+        for t in range(T):
+            for j in range(0, H, 17):
+                acc = 0.0
+                for k in range(K):
+                    s_ = ref["slot"][t, k]
+                    if s_ >= 0:
+                        acc = _rn_f32(Fraction(float(w[t, k])) * Fraction(float(yf[s_, j])) + Fraction(acc))
+                want = torch.tensor([acc], dtype=torch.float32).to(torch.bfloat16).float().item()
+                assert out[t, j] == want or (out[t, j] == 0 and want == 0), (seed, t, j)
