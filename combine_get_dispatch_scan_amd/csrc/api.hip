@@ -5,6 +5,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -92,6 +93,21 @@ int check_handle(const ep_handle_t* h, int min_stage)
 }
 
 }  // namespace
+
+namespace moe_ep {
+
+void debug_launch(const char* kernel, dim3 grid, dim3 block, size_t lds)
+{
+    static const bool on = [] {
+        const char* v = getenv("EP_DEBUG");
+        return v && v[0] && v[0] != '0';
+    }();
+    if (on)
+        fprintf(stderr, "[moe_ep] %s grid=(%u,%u,%u) block=(%u,%u,%u) lds=%zu\n", kernel, grid.x, grid.y,
+                grid.z, block.x, block.y, block.z, lds);
+}
+
+}  // namespace moe_ep
 
 extern "C" {
 

@@ -184,6 +184,7 @@ hipError_t launch_combine_backward(const void* grad_out, const void* y, int T, i
     dim3 block(kBwdWaves * kWave);
 #define EP_BWD(KM)                                                                                   \
     do {                                                                                             \
+        debug_launch(wgrad ? "combine_backward_kernel<wgrad>" : "combine_backward_kernel", grid, block, 0); \
         if (wgrad) hipLaunchKernelGGL((combine_backward_kernel<KM, true>), grid, block, 0, stream, a); \
         else hipLaunchKernelGGL((combine_backward_kernel<KM, false>), grid, block, 0, stream, a);      \
     } while (0)

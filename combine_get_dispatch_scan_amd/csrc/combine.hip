@@ -259,6 +259,7 @@ hipError_t launch_combine_fp8(const void* y, const float* scales, int T, int H, 
     dim3 block(kCombineWaves * kWave);
 #define EP_COMBINE8(KM)                                                                          \
     do {                                                                                         \
+        debug_launch("combine_fp8_kernel", grid, block, 0);                                      \
         if (w) hipLaunchKernelGGL((combine_fp8_kernel<KM, false>), grid, block, 0, stream, a);   \
         else hipLaunchKernelGGL((combine_fp8_kernel<KM, true>), grid, block, 0, stream, a);      \
     } while (0)
@@ -292,6 +293,7 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slo
     dim3 block(kCombineWaves * kWave);
 #define EP_COMBINE(KM)                                                                          \
     do {                                                                                        \
+        debug_launch("combine_kernel", grid, block, 0);                                         \
         if (w) hipLaunchKernelGGL((combine_kernel<KM, false>), grid, block, 0, stream, a);      \
         else hipLaunchKernelGGL((combine_kernel<KM, true>), grid, block, 0, stream, a);         \
     } while (0)

@@ -205,8 +205,11 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
     dim3 grid((unsigned)(a.row_blocks + pad_blocks));
     dim3 block(kDispatchWaves * kWave);
 
-#define EP_DISPATCH(KERNEL, KM, FRESH) \
-    hipLaunchKernelGGL((KERNEL<KM, FRESH>), grid, block, 0, stream, a)
+#define EP_DISPATCH(KERNEL, KM, FRESH)            \
+    do {                                          \
+        debug_launch(#KERNEL, grid, block, 0);    \
+        hipLaunchKernelGGL((KERNEL<KM, FRESH>), grid, block, 0, stream, a); \
+    } while (0)
 #define EP_DISPATCH_K(KERNEL, FRESH)                 \
     do {                                             \
         if (L.K <= 2) EP_DISPATCH(KERNEL, 2, FRESH); \
@@ -247,6 +250,7 @@ hipError_t launch_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStr
     int64_t blocks = (n + 255) / 256;
     if (blocks > 65536)
         blocks = 65536;
+    debug_launch("e4m3fn_encode_kernel", dim3((unsigned)blocks), dim3(256), 0);
     hipLaunchKernelGGL(e4m3fn_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
     return hipGetLastError();
 }

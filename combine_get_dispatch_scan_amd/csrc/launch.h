@@ -6,6 +6,10 @@
 
 namespace moe_ep {
 
+// EP_DEBUG=1 in the environment: every launch prints its kernel, grid, block
+// and dynamic LDS to stderr (read once per process).
+void debug_launch(const char* kernel, dim3 grid, dim3 block, size_t lds);
+
 // get_dispatch_layout: per-chunk count kernel + one-workgroup scan kernel.
 hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, int align,
                          uint8_t* is_token_in_partition, int32_t* pair_code,

@@ -376,6 +376,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, in
                            E, P, align, is_token_in_partition, wide, pair_code, chunk_cnt,     \
                            chunk_base, chunk_pcnt, chunk_inv, expert_offset,                   \
                            num_tokens_per_expert, num_tokens_per_partition, num_invalid, status)
+        debug_launch("layout_single_kernel", grid, block, lds);
         if (K <= 2) EP_LAYOUT1(2);
         else if (K <= 4) EP_LAYOUT1(4);
         else if (K <= 8) EP_LAYOUT1(8);
@@ -389,6 +390,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, in
         hipLaunchKernelGGL(layout_chunk_kernel<KM>, grid, block, lds, stream, topk_idx, \
                            T, K, E, P, is_token_in_partition, wide, pair_code,          \
                            chunk_cnt, chunk_pcnt, chunk_inv)
+        debug_launch("layout_chunk_kernel", grid, block, lds);
         if (K <= 2) EP_LAYOUT(2);
         else if (K <= 4) EP_LAYOUT(4);
         else if (K <= 8) EP_LAYOUT(8);
@@ -400,6 +402,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, in
     }
     const bool staged = (long long)B * (E + P + 1) <= kScanLdsInts;
     const size_t scan_lds = staged ? (size_t)B * (E + P + 1) * sizeof(int) : 0;
+    debug_launch("scan_kernel", dim3(1), dim3(kScanThreads), scan_lds);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), scan_lds, stream, B, E, P, align,
                        chunk_cnt, chunk_base, chunk_pcnt, chunk_inv, expert_offset,
                        num_tokens_per_expert, num_tokens_per_partition, num_invalid, status);

@@ -294,6 +294,7 @@ hipError_t launch_low_latency_dispatch(const LowLatencyLaunch& L, hipStream_t st
     const size_t lds = (size_t)L.E * kLLWaves * sizeof(unsigned long long);
 #define EP_LL(KM)                                                                                \
     do {                                                                                         \
+        debug_launch("low_latency_dispatch_kernel", grid, block, lds);                            \
         if (L.use_fp8) hipLaunchKernelGGL((low_latency_dispatch_kernel<KM, true>), grid, block, lds, stream, a); \
         else hipLaunchKernelGGL((low_latency_dispatch_kernel<KM, false>), grid, block, lds, stream, a);         \
     } while (0)

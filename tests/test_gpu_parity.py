@@ -329,3 +329,70 @@ def test_device_e4m3fn_encoder_exhaustive(ep):
     v = u.view(np.float32)
     got = ep.e4m3fn_encode(torch.from_numpy(v).to(dev)).cpu().numpy()
     assert np.array_equal(got, oracle.e4m3fn_array(v))
+
+
+def test_graph_capture_of_the_dense_path(ep):
+    """layout -> dispatch (FP8) -> combine captured once in a HIP graph (the
+    library records no memset nodes) and replayed on three new batches with
+    eager work between the replays; every replay matches the oracle."""
+    dev = _dev()
+    T, H, K, E, P = 700, 1024, 6, 64, 8
+    cap = T * K
+    s_idx = torch.empty((T, K), dtype=torch.int64, device=dev)
+    s_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    s_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    s_y = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ep.ep_workspace_bytes(T, K, E, P), dtype=torch.uint8, device=dev)
+    ntpp = torch.empty(P, dtype=torch.int32, device=dev)
+    ntpe = torch.empty(E, dtype=torch.int32, device=dev)
+    itip = torch.empty((T, P), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    recv = torch.empty((cap, H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    h = ep.ep_handle_t()
+    p = lambda t: t.data_ptr()
+
+    def step():
+        s = ep._stream()
+        assert ep.ep_get_dispatch_layout(p(s_idx), T, K, E, P, p(ntpp), p(ntpe), p(itip), p(ninv),
+                                         p(ws), ws.numel(), h, s) == ep.EP_OK
+        assert ep.ep_dispatch(p(s_x), p(s_w), H, 1, p(recv), p(sc), cap, h, s) == ep.EP_OK
+        assert ep.ep_combine(p(s_y), h, None, p(out), s) == ep.EP_OK
+
+    cases = []
+    for r in range(4):
+        idx, w = workloads.random_case(600 + r, T, E, K, mask_frac=0.05)
+        cases.append((idx, w, workloads.random_rows(600 + r, T, H, "wide"),
+                      workloads.random_rows(650 + r, cap, H)))
+
+    def load(c):
+        s_idx.copy_(torch.from_numpy(c[0]))
+        s_w.copy_(torch.from_numpy(c[1]))
+        s_x.copy_(_bf16_tensor(c[2], dev))
+        s_y.copy_(_bf16_tensor(c[3], dev))
+
+    load(cases[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                        # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for c in cases[1:]:
+        load(c)
+        junk = torch.randn(1 << 20, device=dev).sum()     # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        idx, w, x, y = c
+        ref = oracle.run_all(idx, w, x, E, P, True, y_bits=y)
+        rows = ref["rows"]
+        assert np.array_equal(ntpe.cpu().numpy(), ref["num_tokens_per_expert"])
+        assert np.array_equal(itip.cpu().numpy(), ref["is_token_in_partition"])
+        assert np.array_equal(recv.cpu().numpy()[:rows], ref["recv_x"])
+        assert np.array_equal(sc.cpu().numpy()[:rows].view(np.uint32), ref["recv_scales"].view(np.uint32))
+        assert np.array_equal(_bits(out), ref["out"])
+        del junk
