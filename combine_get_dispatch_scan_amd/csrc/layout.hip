@@ -12,10 +12,13 @@
 // result does not depend on scheduling); the scan turns the counts into
 // chunk_base and expert_offset.
 //
-// layout_chunk_kernel counts, then the one-workgroup scan_kernel scans.  (A
-// single cooperative launch with a grid barrier in between was measured
-// slower on MI355X: ~22 us for the kernel plus longer launch gaps, against
-// 7 + 7 us for the pair.)
+// layout_chunk_kernel counts, then the one-workgroup scan_kernel scans; a
+// batch of one chunk does both in layout_single_kernel.  Two single-launch
+// forms for several chunks were measured slower on MI355X at the V3 shape:
+// a cooperative launch with a grid barrier (~22 us plus longer launch gaps),
+// and a completion ticket whose last workgroup scans (19.9 us, against 17.7
+// for the pair: each workgroup's agent-scope release fence writes its XCD's
+// L2 back, which costs more than the launch it saves).
 #include "device.h"
 #include "launch.h"
 

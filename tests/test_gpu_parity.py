@@ -151,6 +151,7 @@ SHAPES = [
     (700, 256, 1024, 16, 64, True),
     (1000, 384, 5, 5, 5, True),
     (2049, 4096, 256, 8, 8, True),
+    (33000, 128, 256, 4, 8, True),      # > 128 chunks: separate scan kernel, tables in HBM
 ]
 
 
