@@ -28,19 +28,32 @@ namespace moe_ep {
 #ifndef EP_COMBINE_WAVES
 #define EP_COMBINE_WAVES 4
 #endif
-// Cache policy, measured on MI355X at the V3 shape.  The gathered rows are
-// touched once: non-temporal loads (plain loads cost ~30 us more).  The output
-// rows are written with device-scope (sc1) buffer stores, which write through
-// the XCD's L2: ~176 us, against ~180 us with plain write-back stores and
-// ~182-186 us with non-temporal ones.  The 117 MB of output writes cost far
-// more than their share of bandwidth because they interleave with the 940 MB
-// read stream at the DRAM; the write-through policy spreads them best.
+// Cache policy, measured on MI355X.  The gathered rows are touched once:
+// non-temporal loads (plain loads cost ~30 us more at the V3 shape).
+//
+// Output stores: at the V3 shape (117 MB of output) device-scope (sc1)
+// buffer stores, which write through the XCD's L2, are fastest: ~173 us,
+// against ~182 us with plain write-back or non-temporal stores.  The output
+// writes cost far more than their share of bandwidth because they interleave
+// with the 940 MB read stream at the DRAM; write-through spreads them best.
+//
+// Above EP_COMBINE_STREAM_OUT_BYTES of output the stores are non-temporal
+// instead.  At the large workload (235 MB of output against the 256 MB
+// Infinity Cache) write-through lines stay dirty in the Infinity Cache and
+// are written back during the next call: the next step's dispatch took
+// 282 us after a write-through combine and 218 us after a non-temporal one,
+// while the combine itself went from 366 to 380 us (step 669 -> 618 us).  At
+// V3 the write-through step is faster (294 us against 304 us).
 #ifndef EP_COMBINE_NT_LOAD
 #define EP_COMBINE_NT_LOAD 1
 #endif
 #ifndef EP_COMBINE_STORE_AUX
-#define EP_COMBINE_STORE_AUX 16
+#define EP_COMBINE_STORE_AUX 16                  // sc1
 #endif
+#ifndef EP_COMBINE_STREAM_OUT_BYTES
+#define EP_COMBINE_STREAM_OUT_BYTES (160ll << 20)
+#endif
+constexpr int kCombineStreamAux = 2;             // nt
 
 constexpr int kCombineWaves = EP_COMBINE_WAVES;
 constexpr int kCombineChPerIter = kWave * 8;     // 512 channels per wave step
@@ -56,8 +69,9 @@ struct CombineArgs {
 };
 
 // UNIT: every weight is 1 (the backward of dispatch); fma(1, v, acc) is the
-// exact sum acc + v, so no weights are read.
-template <int KMAX, bool UNIT>
+// exact sum acc + v, so no weights are read.  AUX: cache policy of the
+// output stores.
+template <int KMAX, bool UNIT, int AUX>
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineArgs a)
 {
     const int wi = blockIdx.x * kCombineWaves + threadIdx.x / kWave;
@@ -120,7 +134,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
-                buffer_store16<EP_COMBINE_STORE_AUX>(o, orow, cb * 2);
+                buffer_store16<AUX>(o, orow, cb * 2);
             }
         }
     }
@@ -291,17 +305,24 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slo
     const long long items = (long long)T * a.nseg;
     dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
     dim3 block(kCombineWaves * kWave);
+    const bool stream_out = (long long)T * H * 2 > EP_COMBINE_STREAM_OUT_BYTES;
+#define EP_COMBINE_A(KM, AUX)                                                                   \
+    do {                                                                                        \
+        if (w) hipLaunchKernelGGL((combine_kernel<KM, false, AUX>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((combine_kernel<KM, true, AUX>), grid, block, 0, stream, a);    \
+    } while (0)
 #define EP_COMBINE(KM)                                                                          \
     do {                                                                                        \
-        debug_launch("combine_kernel", grid, block, 0);                                         \
-        if (w) hipLaunchKernelGGL((combine_kernel<KM, false>), grid, block, 0, stream, a);      \
-        else hipLaunchKernelGGL((combine_kernel<KM, true>), grid, block, 0, stream, a);         \
+        debug_launch(stream_out ? "combine_kernel<nt>" : "combine_kernel", grid, block, 0);     \
+        if (stream_out) EP_COMBINE_A(KM, kCombineStreamAux);                                    \
+        else EP_COMBINE_A(KM, EP_COMBINE_STORE_AUX);                                            \
     } while (0)
     if (K <= 2) EP_COMBINE(2);
     else if (K <= 4) EP_COMBINE(4);
     else if (K <= 8) EP_COMBINE(8);
     else EP_COMBINE(16);
 #undef EP_COMBINE
+#undef EP_COMBINE_A
     return hipGetLastError();
 }
 
