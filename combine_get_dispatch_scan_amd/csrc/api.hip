@@ -602,7 +602,10 @@ int ep_recv_counts_decode(const ep_handle_t* handle, const int32_t* host_buf,
             host_counts[i] = off[i + 1] - off[i];
     if (host_num_recv)
         *host_num_recv = off[E];
-    if (handle->stage >= 2 && st[0])
+    // a dense layout drops pairs exactly when N exceeds the capacity, which
+    // also covers a copy taken before dispatch set the drop flag
+    const bool dense = !handle->static_cap && handle->expert_alignment <= 1;
+    if (handle->stage >= 2 && (st[0] || (dense && off[E] > handle->capacity_rows)))
         return fail(EP_ECAPACITY, "dispatch dropped pairs: they did not fit capacity_rows=%d",
                     handle->capacity_rows);
     if (st[1] > 0)

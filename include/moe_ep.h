@@ -318,7 +318,7 @@ int ep_dispatch_backward_fp8(const void* grad_recv, const float* grad_scales,
  *                 a fixed order (per-lane fma chains over the hidden
  *                 dimension, then a 64-lane tree), so results are
  *                 deterministic; against the exact sum the error is at most
- *                 about (H/64 + 6) * 2^-24 * sum_j |grad_out * y|.
+ *                 about (H/64 + 8) * 2^-24 * sum_j |grad_out * y|.
  * Errors: EP_EINVAL, EP_EHIP.
  */
 int ep_combine_backward(const void* grad_out, const void* y, const ep_handle_t* handle,
@@ -345,6 +345,14 @@ int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts,
  * Once the stream has passed this point (the caller waits on an event
  * recorded after it, or on the stream), ep_recv_counts_decode gives the same
  * results and return code as ep_handle_recv_counts.
+ * The counts are final once the layout has run.  For a dense layout
+ * (ep_get_dispatch_layout, or alignment 1) the copy may therefore be taken
+ * right after the layout call, e.g. on a second stream that waits for it, so
+ * that it overlaps dispatch: ep_recv_counts_decode then detects dropped pairs
+ * from N > capacity_rows of the dispatched handle.  (On MI355X with ROCm 7
+ * the cross-stream wait costs more than the small copy it hides, so the
+ * same-stream copy after dispatch is the faster default.)  For aligned and
+ * low-latency layouts the drop flag is written by dispatch: copy after it.
  * Errors: EP_EINVAL, EP_EHIP.
  */
 int ep_handle_recv_counts_async(const ep_handle_t* handle, int32_t* host_buf, hipStream_t stream);

@@ -180,6 +180,16 @@ def test_recv_counts_decode_on_host():
         rc = ep.ep_recv_counts_decode(h, buf, counts, ctypes.byref(n))
         assert rc == want, (status, rc)
         assert list(counts) == [3, 1, 1, 2, 0, 2] and n.value == 9
+    # a dense layout's drops also follow from N > capacity_rows (a copy taken
+    # before dispatch set the flag); aligned layouts rely on the flag alone
+    h.capacity_rows = 8
+    buf = (ctypes.c_int32 * (E + 5))(*(off + [0, 0, 9, 0]))
+    assert ep.ep_recv_counts_decode(h, buf, None, None) == ep.EP_ECAPACITY
+    h.expert_alignment = 4
+    assert ep.ep_recv_counts_decode(h, buf, None, None) == ep.EP_OK
+    h.expert_alignment = 1
+    h.static_cap = 3
+    assert ep.ep_recv_counts_decode(h, buf, None, None) == ep.EP_OK
     # before dispatch the overflow word is not consulted
     h1 = _fake_handle(stage=1, E=E, P=3)
     buf = (ctypes.c_int32 * (E + 5))(*(off + [1, 0, 9, 0]))

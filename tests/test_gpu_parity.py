@@ -294,6 +294,36 @@ def test_async_counts_match_sync(ep):
         assert np.array_equal(np.array(a[0]), np.bincount(idx[idx >= 0], minlength=wl.E))
 
 
+def test_counts_copied_before_dispatch_on_a_side_stream(ep):
+    """For a dense layout the counts can be read back right after the layout,
+    on a second stream, overlapping dispatch; the decode still reports drops
+    (N > capacity) once the handle is dispatched."""
+    dev = _dev()
+    wl = workloads.config("v3")
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    t_idx, t_w, t_x = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev), _bf16_tensor(x, dev)
+    for cap in (wl.T * wl.K, N - 1000):
+        lay = ep.get_dispatch_layout(t_idx, wl.E, wl.P)
+        laid = torch.cuda.Event()
+        laid.record(main)
+        buf = torch.full((wl.E + 5,), -9, dtype=torch.int32, pin_memory=True)
+        side.wait_event(laid)
+        with torch.cuda.stream(side):
+            ep.handle_recv_counts_async(lay.handle, buf)
+            ready = torch.cuda.Event()
+            ready.record(side)
+        recv, sc, h = ep.dispatch(t_x, t_w, lay, True, capacity_rows=cap)
+        ready.synchronize()
+        counts, n, st = ep.recv_counts_decode(h, buf)
+        torch.cuda.synchronize()
+        assert n == N and st == (ep.EP_OK if cap >= N else ep.EP_ECAPACITY)
+        assert np.array_equal(np.array(counts), np.bincount(idx[idx >= 0], minlength=wl.E))
+        assert (counts, n, st) == ep.handle_recv_counts(h)
+
+
 def test_determinism(ep):
     wl = workloads.config("skewed")
     idx, w, x = workloads.make(wl)
