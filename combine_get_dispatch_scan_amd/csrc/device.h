@@ -12,12 +12,12 @@ constexpr int kChunkWaves = kChunk / kWave;
 constexpr int kQBlock = 128;       // channels per FP8 scale
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Work split of a row-streaming kernel: each token row has `iters` wave
-// steps; a work item (one wave) takes `iters_per_item` consecutive steps of
-// one row.  Rows are split only as far as needed to give the launch at least
-// `min_items` work items, so the last round of waves is short.
+// steps; a work item (one wave) takes `iters_per_seg` consecutive steps of
+// one row (a segment; `nseg` segments per row).  Rows are split only as far
+// as needed to give the launch at least `min_items` work items and no item
+// more than `max_iters_per_item` steps.
 struct RowSplit {
     int nseg, iters_per_seg;
 };
@@ -86,11 +86,6 @@ __device__ __forceinline__ void buffer_store16(u32x4 v, __amdgpu_buffer_rsrc_t r
     __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, AUX);
 }
 
-__device__ __forceinline__ u32x4 load16(const void* p)
-{
-    return *reinterpret_cast<const u32x4*>(p);
-}
-
 // BF16 <-> fp32.  Widening is exact; narrowing rounds to nearest, ties to
 // even, on the 16 dropped bits (operands are finite by contract).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -134,8 +129,9 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float v)
 
 // Two OCP E4M3FN codes (bytes 0,1 or, with HI, bytes 2,3 of w) -> their exact
 // fp32 values, with gfx950's converter (v_cvt_pk_f32_fp8).  It decodes the OCP
-// format exactly -- subnormals m * 2^-9, 0x7F / 0xFF as NaN -- which a device
-// test checks against the formula on all 256 codes.
+// format exactly -- subnormals m * 2^-9, 0x7F / 0xFF as NaN: a probe compared
+// all 256 codes with the formula, and a device test keeps checking the 254
+// finite ones through the FP8 combine.
 template <bool HI>
 __device__ __forceinline__ void e4m3fn_pair_to_f32(uint32_t w, float& a, float& b)
 {
