@@ -96,6 +96,21 @@ __device__ __forceinline__ void pad_item(const DispatchArgs& a, bool fp8)
     zero_row(a.recv, a.scales, row, a.H, fp8, a.scale_ld);
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (hardware workgroup b runs
+// on XCD b % 8).  FP8 rows remap them so that each XCD takes one contiguous
+// eighth of the row work: the 32-byte scale pieces that the segments of one
+// receive row write then meet in the same L2 and leave it as whole lines.
+// Measured at the V3 shape: 94.5-95 us against 97.5-98 us for the plain
+// order (large workload: 202 against 211 us).  The tail past the last full
+// group of 8 keeps its order.
+__device__ __forceinline__ int xcd_contiguous_block(int b, int row_blocks)
+{
+    const int per = row_blocks / 8;
+    if (b >= 8 * per)
+        return b;
+    return (b % 8) * per + b / 8;
+}
+
 template <int KMAX>
 __device__ __forceinline__ void row_slots(const DispatchArgs& a, int s_own, int (&sk)[KMAX])
 {
@@ -111,7 +126,7 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(Di
         pad_item(a, true);
         return;
     }
-    const int wi = blockIdx.x * kDispatchWaves + threadIdx.x / kWave;
+    const int wi = xcd_contiguous_block(blockIdx.x, a.row_blocks) * kDispatchWaves + threadIdx.x / kWave;
     const int t = wi / a.nseg;
     const int seg = wi % a.nseg;
     if (t >= a.T)
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8in_kernel(
         pad_item(a, true);
         return;
     }
-    const int wi = blockIdx.x * kDispatchWaves + threadIdx.x / kWave;
+    const int wi = xcd_contiguous_block(blockIdx.x, a.row_blocks) * kDispatchWaves + threadIdx.x / kWave;
     const int t = wi / a.nseg;
     const int seg = wi % a.nseg;
     if (t >= a.T)
