@@ -119,21 +119,26 @@ def cpu_baseline(wl, idx, w, x, y, runs):
 
 
 def bench_low_latency(args):
+    wl_T = __import__("workloads").config(args.config).T
+    if wl_T > 256:
+        print(f"--low-latency takes at most 256 tokens ({args.config} has {wl_T})", file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(measure_low_latency(args.config, args.ll_cap, args.steps, args.warmup)), flush=True)
+
+
+def measure_low_latency(config, ll_cap, steps, warmup):
     """Decode step through the one-launch dispatch: ep_low_latency_dispatch ->
     counts readback -> ep_combine, timed eagerly and as a replayed HIP graph
-    (dispatch + combine captured once)."""
+    (dispatch + combine captured once).  Returns the JSON record."""
     import torch
     import combine_get_dispatch_scan_amd as ep
     import workloads
 
     ep.load()
     dev = torch.device("cuda:0")
-    wl = workloads.config(args.config)
+    wl = workloads.config(config)
     T, H, K, E, P = wl.T, wl.H, wl.K, wl.E, wl.P
-    if T > 256:
-        print(f"--low-latency takes at most 256 tokens ({args.config} has {T})", file=sys.stderr)
-        sys.exit(2)
-    cap = args.ll_cap or T
+    cap = ll_cap or T
     idx, w, x = workloads.make(wl)
     N = int((idx >= 0).sum())
     y = workloads.expert_outputs(wl, E * cap)
@@ -175,16 +180,16 @@ def bench_low_latency(args):
         if rc != 0:
             raise RuntimeError(ep.ep_last_error())
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     assert nrecv.value == N, (nrecv.value, N)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step()
     torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
 
     # kernel duration: back-to-back launches keep the GPU busy, so events
     # around a batch time the kernels rather than the host's launch gaps
@@ -219,15 +224,15 @@ def bench_low_latency(args):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fwd()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         g.replay()
     torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    print(f"[bench] low-latency {args.config}: {ms_per_step * 1e3:.1f} us/step eager, "
+    graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+    print(f"[bench] low-latency {config}: {ms_per_step * 1e3:.1f} us/step eager, "
           f"{graph_ms * 1e3:.1f} us/step graph, kernels: dispatch {disp_us:.2f} us, "
           f"combine {comb_us:.2f} us",
           file=sys.stderr, flush=True)
@@ -243,11 +248,11 @@ def bench_low_latency(args):
     value = (disp_logical + comb_logical) / (ms_per_step * 1e-3) / 1e9
     res = {
         "metric": "low-latency dispatch & combine logical GB/s on 1 MI355X",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3+bf16/fp32-acc" if wl.use_fp8 else "bf16/fp32-acc", "data": "synthetic",
-        "config": {"workload": DESCR[args.config] + ", one-launch static-capacity dispatch",
+        "config": {"workload": DESCR[config] + ", one-launch static-capacity dispatch",
                    "tokens": T, "hidden": H, "experts": E, "topk": K, "partitions": P,
                    "dispatched_pairs": N, "rows_per_expert": cap},
         "graph_replay_us_per_step": round(graph_ms * 1e3, 2),
@@ -257,9 +262,9 @@ def bench_low_latency(args):
                      "achieved": round(disp_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(disp_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": disp_alg,
                      "avg_launch_us": round(disp_ms * 1e3, 2),
-                     "traffic": measured_traffic(f"{args.config}_low_latency", "low_latency_dispatch_kernel")},
+                     "traffic": measured_traffic(f"{config}_low_latency", "low_latency_dispatch_kernel")},
     }
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def main():
@@ -521,6 +526,14 @@ def main():
             "combine": round(bc["combine_alg"] / (phases["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
     }
+
+    if args.config == "v3":
+        # the decode-shape path through the one-launch dispatch, for reference
+        ll = measure_low_latency("decode", 0, 50, 10)
+        res["low_latency_decode"] = {
+            "workload": ll["config"]["workload"], "us_per_step": round(ll["ms_per_step"] * 1e3, 2),
+            "graph_replay_us_per_step": ll["graph_replay_us_per_step"], "kernels_us": ll["kernels_us"],
+            "dispatch_roofline_frac": ll["roofline"]["frac"]}
 
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_runs} oracle runs)", file=sys.stderr, flush=True)
