@@ -73,7 +73,8 @@ def test_round_trip_from_dispatch(ep, name):
 
 
 @pytest.mark.parametrize("T,H,K,E,mask", [(64, 128, 1, 8, 0.0), (100, 1152, 6, 32, 0.1),
-                                          (37, 7168, 8, 256, 0.2), (256, 2048, 16, 64, 0.05)])
+                                          (37, 7168, 8, 256, 0.2), (256, 2048, 16, 64, 0.05),
+                                          (4, 32768, 4, 8, 0.0)])
 def test_every_code_random_scales(ep, T, H, K, E, mask):
     dev = _dev()
     idx, w = workloads.random_case(400 + T, T, E, K, mask_frac=mask)

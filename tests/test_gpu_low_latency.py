@@ -148,6 +148,7 @@ def test_decode_workload_fp8():
     (256, 4096, 16, 1024, 64, 2, False, "clean"),
     (256, 7168, 8, 256, 8, 64, False, "clean"),
     (129, 512, 2, 8, 2, 200, True, "dup"),
+    (7, 32768, 4, 16, 4, 3, True, "clean"),          # maximum hidden size
 ])
 def test_shapes_and_edge_cases(T, H, K, E, P, cap, use_fp8, kind):
     ep = pytest.importorskip("combine_get_dispatch_scan_amd")

@@ -152,6 +152,8 @@ SHAPES = [
     (1000, 384, 5, 5, 5, True),
     (2049, 4096, 256, 8, 8, True),
     (33000, 128, 256, 4, 8, True),      # > 128 chunks: separate scan kernel, tables in HBM
+    (3, 32768, 16, 8, 4, True),         # maximum hidden size
+    (5, 32760, 16, 16, 16, False),      # maximum BF16 hidden (a multiple of 8), K = E
 ]
 
 
