@@ -1,0 +1,115 @@
+"""The oracle's pins must catch plausible mistakes: each case below plants
+one mistake in a copy of oracle.c (a dropped term, a wrong index or bound, a
+transposed operand, a wrong constant), builds it into its own library, points
+the oracle at it and runs the pins that cover that function.  At least one
+of them has to fail.  The mutants only change arithmetic or indices inside
+the arrays' bounds, so a mutant cannot write out of bounds."""
+import ctypes  # noqa: F401  (the oracle loads through ctypes)
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+C = pins.CASES
+
+MUTANTS = [
+    ("bf16 rounding: tie-to-even term dropped",
+     "uint32_t r = u + 0x7FFFu + lsb;", "uint32_t r = u + 0x7FFFu;",
+     [pins.test_bf16_rne_matches_torch_on_random_and_ties]),
+    ("e4m3: saturates to the NaN code",
+     "return sign | 0x7E;                 /* satfinite: +-448            */",
+     "return sign | 0x7F;",
+     [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest]),
+    ("e4m3: truncates instead of rounding",
+     "double n = nearbyint(a / quantum);", "double n = floor(a / quantum);",
+     [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest]),
+    ("e4m3: subnormal range boundary off by one binade",
+     "    if (lead < -6)\n        lead = -6;", "    if (lead < -7)\n        lead = -7;",
+     [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest]),
+    ("e4m3 decode: subnormal quantum 2^-10",
+     "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);",
+     [pins.test_e4m3fn_decode_roundtrip_and_bound]),
+    ("quantisation: inverse scale transposed",
+     "float inv = 448.0f / a;", "float inv = a / 448.0f;",
+     [lambda: pins.test_quant_block_properties("normal"), pins.test_quant_block_special_cases]),
+    ("quantisation: scale inverted",
+     "float s = a / 448.0f;", "float s = 448.0f / a;",
+     [lambda: pins.test_quant_block_properties("normal"), pins.test_quant_block_special_cases]),
+    ("layout: repeated ids not rejected",
+     "} else if (e >= E || seen[e]) {", "} else if (e >= E) {",
+     [lambda: pins.test_layout_and_slots_against_independent_definitions(C[3], "dirty")]),
+    ("layout: partition index e % P",
+     "is_token_in_partition[(size_t)t * P + e / epp] = 1;",
+     "is_token_in_partition[(size_t)t * P + e % P] = 1;",
+     [lambda: pins.test_layout_and_slots_against_independent_definitions(C[4], "clean")]),
+    ("layout: invalid ids not counted",
+     "                ok = 0;                               /* invalid         */\n                ninv++;",
+     "                ok = 0;                               /* invalid         */",
+     [lambda: pins.test_layout_and_slots_against_independent_definitions(C[3], "dirty")]),
+    ("offsets: running term dropped",
+     "off[e + 1] = off[e] + num_tokens_per_expert[e];", "off[e + 1] = num_tokens_per_expert[e];",
+     [lambda: pins.test_layout_and_slots_against_independent_definitions(C[2], "clean")]),
+    ("aligned offsets: rounded down",
+     "off[e + 1] = off[e] + ((c + A - 1) / A) * A;", "off[e + 1] = off[e] + (c / A) * A;",
+     [lambda: pins.test_aligned_offsets_closed_form(64)]),
+    ("slots: wrong source token",
+     "src_token[s] = t;", "src_token[s] = t > 0 ? t - 1 : 0;",
+     [lambda: pins.test_layout_and_slots_against_independent_definitions(C[2], "clean")]),
+    ("slots: capacity bound off by one",
+     "if (s < capacity) {", "if (s < capacity - 1) {",
+     [pins.test_dispatch_capacity_drops_rows]),
+    ("static slots: row off by one",
+     "slot[i] = (int32_t)e * cap + r;", "slot[i] = (int32_t)e * cap + r + (r + 1 < cap);",
+     [lambda: pins.test_static_slots_against_stable_sort(128, 256, 8, 16, "clean")]),
+    ("dispatch: only the first block's scale copied",
+     "memcpy(scales + (size_t)r * nb, s, sizeof(float) * (size_t)nb);",
+     "memcpy(scales + (size_t)r * nb, s, sizeof(float));",
+     [lambda: pins.test_dispatch_rows_are_the_source_rows(True)]),
+    ("combine: accumulation dropped",
+     "acc = fmaf(w[(size_t)t * K + k], oracle_bf16_to_f32(y[(size_t)r * H + j]), acc);",
+     "acc = fmaf(w[(size_t)t * K + k], oracle_bf16_to_f32(y[(size_t)r * H + j]), 0.0f);",
+     [pins.test_combine_pow2_weights_exact, pins.test_combine_within_one_ulp_of_exact_sum]),
+    ("combine: weight index transposed",
+     "acc = fmaf(w[(size_t)t * K + k], oracle_bf16_to_f32(y[(size_t)r * H + j]), acc);",
+     "acc = fmaf(w[(size_t)k * T + t], oracle_bf16_to_f32(y[(size_t)r * H + j]), acc);",
+     [pins.test_combine_pow2_weights_exact, pins.test_combine_within_one_ulp_of_exact_sum]),
+    ("FP8 combine: scale of the wrong block",
+     "scales[(size_t)r * nb + j / 128]", "scales[(size_t)r * nb + j % nb]",
+     [pins.test_combine_fp8_single_pair_matches_torch_dequant]),
+    ("dispatch backward: running sum dropped",
+     "acc = acc + oracle_bf16_to_f32(grad_recv[(size_t)r * H + j]);",
+     "acc = oracle_bf16_to_f32(grad_recv[(size_t)r * H + j]);",
+     [lambda: pins.test_dispatch_backward_is_the_adjoint_of_dispatch(33, 8, 3, 2, 16)]),
+    ("combine backward: weight dropped from grad_y",
+     "grad_y[(size_t)r * H + j] = oracle_bf16_rne(wk * oracle_bf16_to_f32(g[j]));",
+     "grad_y[(size_t)r * H + j] = oracle_bf16_rne(oracle_bf16_to_f32(g[j]));",
+     [lambda: pins.test_combine_backward_grad_y_is_the_adjoint_of_combine(40, 8, 3, 2, 16)]),
+    ("combine backward: grad_w from the weight instead of y",
+     "(double)oracle_bf16_to_f32(y[(size_t)r * H + j]);",
+     "(double)wk;",
+     [pins.test_combine_backward_grad_w_matches_finite_differences]),
+]
+
+
+@pytest.mark.parametrize("name,orig,new,checks", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_the_mutant(name, orig, new, checks, tmp_path, monkeypatch):
+    src = open(oracle._SRC).read()
+    assert src.count(orig) == 1, f"mutation site not unique: {orig!r}"
+    mutated = tmp_path / "oracle.c"
+    mutated.write_text(src.replace(orig, new))
+    (tmp_path / "oracle.h").write_text(open(os.path.join(os.path.dirname(oracle._SRC), "oracle.h")).read())
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                    "-shared", "-o", str(so), str(mutated), "-lm"], check=True)
+    monkeypatch.setattr(oracle, "LIB_PATH", str(so))
+    monkeypatch.setattr(oracle, "_lib", None)
+    caught = []
+    for check in checks:
+        try:
+            check()
+        except AssertionError:
+            caught.append(getattr(check, "__name__", "check"))
+    assert caught, f"no pin caught the mutant: {name}"
