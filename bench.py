@@ -318,8 +318,9 @@ def main():
 
     def step(ev=None, dom=None):
         """One pass of the path.  ev: 4 events around the three calls, or
-        (with dom) 2 events around the dominant call only."""
-        if ev is not None and dom is None:
+        (with dom) 2 events around the dominant call only, or (dom "all") 2
+        events around the whole step."""
+        if ev is not None and dom in (None, "all"):
             ev[0].record(stream)
         rc = ep.ep_get_dispatch_layout(p(t_idx), T, K, E, P, p(ntpp), p(ntpe), p(itip), p(ninv),
                                        p(ws), ws.numel(), h, sp)
@@ -341,6 +342,8 @@ def main():
             ev[1].record(stream)
         if ev is not None and dom is None:
             ev[3].record(stream)
+        if dom == "all":
+            ev[1].record(stream)
         # the grouped GEMM would need the counts here; combine is already queued
         counts_ready.synchronize()
         rc |= ep.ep_recv_counts_decode(h, host_buf.data_ptr(), counts, ctypes.byref(nrecv))
@@ -383,6 +386,18 @@ def main():
                  "p90": round(dom_all[min(len(dom_all) - 1, int(0.9 * len(dom_all)))] * 1e3, 2)}
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {dom} {dom_ms * 1e3:.2f} us",
           file=sys.stderr, flush=True)
+
+    # cold steps: reading a 2 GiB scratch buffer before each step evicts the
+    # Infinity Cache (256 MB) and the L2s with clean lines (a fill would leave
+    # dirty ones for the step to write back); two events bracket the step
+    scratch = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    for e in cold_ev:
+        scratch.amax()
+        step(e, "all")
+    torch.cuda.synchronize()
+    cold_us = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in cold_ev)
+    del scratch
 
     bc = byte_counts(wl, N)
     dom_bytes = bc["dispatch_alg"] if dom == "dispatch" else bc["combine_alg"]
@@ -513,6 +528,8 @@ def main():
             "traffic": measured_traffic(args.config, dom_kernel),
         },
         "phases_us": {k: round(v * 1e3, 2) for k, v in phases.items()},
+        "cold_step_us": {"median": round(cold_us[len(cold_us) // 2], 2), "min": round(cold_us[0], 2),
+                         "note": "each step after reading a 2 GiB scratch buffer, events around the step"},
         "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},
         "backward": backward,
         "gemm_layout": gemm,
