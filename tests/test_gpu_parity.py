@@ -429,3 +429,52 @@ def test_graph_capture_of_the_dense_path(ep):
         assert np.array_equal(sc.cpu().numpy()[:rows].view(np.uint32), ref["recv_scales"].view(np.uint32))
         assert np.array_equal(_bits(out), ref["out"])
         del junk
+
+
+def test_two_host_threads_on_two_streams(ep):
+    """The library keeps no shared mutable state (the last-error string is per
+    thread, workspaces and handles belong to the caller): two host threads,
+    each on its own stream and workspace, run the path concurrently and each
+    gets the oracle's result."""
+    import threading
+    dev = _dev()
+    jobs = []
+    for j, (T, H, E, K, P, fp8) in enumerate([(1500, 1024, 64, 6, 8, True), (900, 776, 32, 4, 4, False)]):
+        idx, w = workloads.random_case(800 + j, T, E, K, mask_frac=0.05)
+        x = workloads.random_rows(810 + j, T, H, "wide" if fp8 else "normal")
+        ref = oracle.run_all(idx, w, x, E, P, fp8)
+        y = workloads.random_rows(820 + j, ref["rows"], H)
+        jobs.append(dict(args=(idx, w, x, y, E, P, fp8), ref=ref, ref_out=oracle.combine(y, ref["slot"], w)))
+    errors = []
+
+    def worker(job):
+        try:
+            idx, w, x, y, E, P, fp8 = job["args"]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                t_idx = torch.from_numpy(idx).to(dev)
+                t_w = torch.from_numpy(w).to(dev)
+                t_x = _bf16_tensor(x, dev)
+                t_y = _bf16_tensor(y, dev)
+                for _ in range(5):
+                    lay = ep.get_dispatch_layout(t_idx, E, P)
+                    recv, sc, h = ep.dispatch(t_x, t_w, lay, fp8)
+                    out = ep.combine(t_y, h)
+                s.synchronize()
+                rows = job["ref"]["rows"]
+                got = recv.view(torch.uint8).cpu().numpy() if fp8 else _bits(recv)
+                assert np.array_equal(got[:rows], job["ref"]["recv_x"])
+                assert np.array_equal(h.slot.cpu().numpy(), job["ref"]["slot"])
+                assert np.array_equal(_bits(out), job["ref_out"])
+                # an error on this thread leaves the other thread's message alone
+                assert ep.ep_dispatch(None, None, 0, 0, None, None, 0, ep.ep_handle_t(), None) == ep.EP_EINVAL
+        except Exception as e:      # surfaced by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
