@@ -81,6 +81,7 @@ __device__ __forceinline__ int pair_slot(const DispatchArgs& a, int t, int seg)
 // one wave per (expert, padding row index < align - 1).  Expert e's block is
 // [expert_offset[e], expert_offset[e+1]) and its rows from expert_offset[e] +
 // count(e) on are padding; count(e) is the last chunk's base plus its count.
+template <bool NT>
 __device__ __forceinline__ void pad_item(const DispatchArgs& a, bool fp8)
 {
     const int item = (blockIdx.x - a.row_blocks) * kDispatchWaves + threadIdx.x / kWave;
@@ -93,7 +94,7 @@ __device__ __forceinline__ void pad_item(const DispatchArgs& a, bool fp8)
     const int row = a.expert_offset[e] + cnt + item % per;
     if (row >= a.expert_offset[e + 1] || row >= a.capacity)
         return;
-    zero_row(a.recv, a.scales, row, a.H, fp8, a.scale_ld);
+    zero_row<NT>(a.recv, a.scales, row, a.H, fp8, a.scale_ld);
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (hardware workgroup b runs
@@ -119,11 +120,11 @@ __device__ __forceinline__ void row_slots(const DispatchArgs& a, int s_own, int 
         sk[k] = k < a.K ? readlane(s_own, k) : -1;
 }
 
-template <int KMAX, bool FRESH>
+template <int KMAX, bool FRESH, bool NTS>
 __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(DispatchArgs a)
 {
     if ((int)blockIdx.x >= a.row_blocks) {
-        pad_item(a, true);
+        pad_item<NTS>(a, true);
         return;
     }
     const int wi = xcd_contiguous_block(blockIdx.x, a.row_blocks) * kDispatchWaves + threadIdx.x / kWave;
@@ -135,15 +136,15 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8_kernel(Di
     row_slots<KMAX>(a, pair_slot<KMAX, FRESH>(a, t, seg), sk);
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
-    fp8_rows<KMAX>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end, a.scale_ld,
+    fp8_rows<KMAX, NTS>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end, a.scale_ld,
                    static_cast<uint8_t*>(a.recv), a.scales);
 }
 
-template <int KMAX, bool FRESH>
+template <int KMAX, bool FRESH, bool NTS>
 __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8in_kernel(DispatchArgs a)
 {
     if ((int)blockIdx.x >= a.row_blocks) {
-        pad_item(a, true);
+        pad_item<NTS>(a, true);
         return;
     }
     const int wi = xcd_contiguous_block(blockIdx.x, a.row_blocks) * kDispatchWaves + threadIdx.x / kWave;
@@ -155,16 +156,16 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_fp8in_kernel(
     row_slots<KMAX>(a, pair_slot<KMAX, FRESH>(a, t, seg), sk);
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
-    fp8in_rows<KMAX>(reinterpret_cast<const uint8_t*>(a.x) + (size_t)t * a.H,
+    fp8in_rows<KMAX, NTS>(reinterpret_cast<const uint8_t*>(a.x) + (size_t)t * a.H,
                      a.x_scales + (size_t)t * (a.H / kQBlock), sk, a.H, i_begin, i_end, a.scale_ld,
                      static_cast<uint8_t*>(a.recv), a.scales);
 }
 
-template <int KMAX, bool FRESH>
+template <int KMAX, bool FRESH, bool NTS>
 __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_bf16_kernel(DispatchArgs a)
 {
     if ((int)blockIdx.x >= a.row_blocks) {
-        pad_item(a, false);
+        pad_item<NTS>(a, false);
         return;
     }
     const int wi = blockIdx.x * kDispatchWaves + threadIdx.x / kWave;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_bf16_kernel(D
     row_slots<KMAX>(a, pair_slot<KMAX, FRESH>(a, t, seg), sk);
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
-    bf16_rows<KMAX>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end,
+    bf16_rows<KMAX, NTS>(a.x + (size_t)t * a.H, sk, a.H, i_begin, i_end,
                     static_cast<uint16_t*>(a.recv));
 }
 
@@ -220,10 +221,16 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
     dim3 grid((unsigned)(a.row_blocks + pad_blocks));
     dim3 block(kDispatchWaves * kWave);
 
-#define EP_DISPATCH(KERNEL, KM, FRESH)            \
-    do {                                          \
-        debug_launch(#KERNEL, grid, block, 0);    \
-        hipLaunchKernelGGL((KERNEL<KM, FRESH>), grid, block, 0, stream, a); \
+    // receive buffers that fit the Infinity Cache: plain stores (see the
+    // cache hints in dispatch_rows.h)
+    const long long recv_bytes =
+        (long long)L.capacity * L.H * (L.use_fp8 ? 1 : 2) + (L.use_fp8 ? (long long)L.capacity * (L.H / kQBlock) * 4 : 0);
+    const bool nt_store = EP_DISPATCH_NT_STORE && recv_bytes > EP_DISPATCH_CACHED_RECV_BYTES;
+#define EP_DISPATCH(KERNEL, KM, FRESH)                                                  \
+    do {                                                                                \
+        debug_launch(nt_store ? #KERNEL "<nt>" : #KERNEL, grid, block, 0);              \
+        if (nt_store) hipLaunchKernelGGL((KERNEL<KM, FRESH, true>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((KERNEL<KM, FRESH, false>), grid, block, 0, stream, a);         \
     } while (0)
 #define EP_DISPATCH_K(KERNEL, FRESH)                 \
     do {                                             \

@@ -27,12 +27,18 @@ namespace moe_ep {
 #endif
 // Cache hints of the row traffic.  Measured on MI355X at the V3 shape: plain
 // loads of x with non-temporal stores of the received rows is fastest (~98 us
-// against ~125 us with both non-temporal and ~138 us with plain stores).
+// against ~125 us with both non-temporal and ~138 us with plain stores).  A
+// receive buffer that fits the 256 MB Infinity Cache is written with plain
+// stores instead (the dispatch launcher decides): 36 against 39 us for the
+// skewed workload's 191 MB, and its step 98 against 101 us.
 #ifndef EP_DISPATCH_NT_LOAD
 #define EP_DISPATCH_NT_LOAD 0
 #endif
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 1
+#endif
+#ifndef EP_DISPATCH_CACHED_RECV_BYTES
+#define EP_DISPATCH_CACHED_RECV_BYTES (256ll << 20)
 #endif
 
 constexpr int kDispatchWaves = EP_DISPATCH_WAVES;   // waves per workgroup
@@ -53,7 +59,7 @@ __device__ __forceinline__ size_t scale_index(int r, int b, int nb, int scale_ld
 // codes and block scales to the receive rows sk[].  Called by the whole wave:
 // lanes past the row end (active false) hold zeros and only join the amax
 // reduction.
-template <int KMAX>
+template <int KMAX, bool NT = EP_DISPATCH_NT_STORE>
 __device__ __forceinline__ void fp8_step_store(const u32x4& lo, const u32x4& hi, int cb, bool active,
                                                const int (&sk)[KMAX], int H, int scale_ld,
                                                uint8_t* __restrict__ recv, float* __restrict__ scales)
@@ -90,7 +96,7 @@ __device__ __forceinline__ void fp8_step_store(const u32x4& lo, const u32x4& hi,
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (sk[k] >= 0) {
-                store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, q);
+                store16_hint<NT>(recv + (size_t)sk[k] * H + cb, q);
                 if ((lane & 7) == 0)
                     scales[scale_index(sk[k], blk, nb, scale_ld)] = scale;
             }
@@ -114,7 +120,7 @@ __device__ __forceinline__ bool fp8_step_load(const uint16_t* __restrict__ xrow,
 }
 
 // x[t] row -> K receive rows over wave steps [i_begin, i_end) of 1024 channels
-template <int KMAX>
+template <int KMAX, bool NT>
 __device__ __forceinline__ void fp8_rows(const uint16_t* __restrict__ xrow, const int (&sk)[KMAX],
                                          int H, int i_begin, int i_end, int scale_ld,
                                          uint8_t* __restrict__ recv, float* __restrict__ scales)
@@ -137,25 +143,25 @@ __device__ __forceinline__ void fp8_rows(const uint16_t* __restrict__ xrow, cons
         for (int u = 0; u < kDispatchUnroll; ++u) {
             if (i0 + u >= i_end)
                 break;
-            fp8_step_store<KMAX>(lo[u], hi[u], (i0 + u) * kFp8ChPerIter + lane * 16, act[u], sk, H,
-                                 scale_ld, recv, scales);
+            fp8_step_store<KMAX, NT>(lo[u], hi[u], (i0 + u) * kFp8ChPerIter + lane * 16, act[u], sk,
+                                     H, scale_ld, recv, scales);
         }
     }
 }
 
 // Store one BF16 wave step (lane: 8 channels from cb) to the receive rows sk[].
-template <int KMAX>
+template <int KMAX, bool NT = EP_DISPATCH_NT_STORE>
 __device__ __forceinline__ void bf16_step_store(const u32x4& d, int cb, const int (&sk)[KMAX], int H,
                                                 uint16_t* __restrict__ recv)
 {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         if (sk[k] >= 0)
-            store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, d);
+            store16_hint<NT>(recv + (size_t)sk[k] * H + cb, d);
 }
 
 // x[t] row -> K receive rows over wave steps [i_begin, i_end) of 512 channels
-template <int KMAX>
+template <int KMAX, bool NT>
 __device__ __forceinline__ void bf16_rows(const uint16_t* __restrict__ xrow, const int (&sk)[KMAX],
                                           int H, int i_begin, int i_end,
                                           uint16_t* __restrict__ recv)
@@ -173,14 +179,14 @@ __device__ __forceinline__ void bf16_rows(const uint16_t* __restrict__ xrow, con
         for (int u = 0; u < kDispatchUnroll; ++u) {
             const int cb = (i0 + u) * kBf16ChPerIter + lane * 8;
             if (i0 + u < i_end && cb < H)
-                bf16_step_store<KMAX>(d[u], cb, sk, H, recv);
+                bf16_step_store<KMAX, NT>(d[u], cb, sk, H, recv);
         }
     }
 }
 
 // Pre-quantised input: the token's E4M3FN codes (16 per lane, 1024 channels
 // per wave step) and its block scales are copied to the receive rows sk[].
-template <int KMAX>
+template <int KMAX, bool NT>
 __device__ __forceinline__ void fp8in_rows(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
                                            const int (&sk)[KMAX], int H, int i_begin, int i_end,
                                            int scale_ld, uint8_t* __restrict__ recv,
@@ -207,7 +213,7 @@ __device__ __forceinline__ void fp8in_rows(const uint8_t* __restrict__ xq, const
 #pragma unroll
                 for (int k = 0; k < KMAX; ++k) {
                     if (sk[k] >= 0) {
-                        store16_hint<EP_DISPATCH_NT_STORE>(recv + (size_t)sk[k] * H + cb, d[u]);
+                        store16_hint<NT>(recv + (size_t)sk[k] * H + cb, d[u]);
                         if ((lane & 7) == 0)
                             scales[scale_index(sk[k], blk, nb, scale_ld)] = sc[u];
                     }
@@ -219,6 +225,7 @@ __device__ __forceinline__ void fp8in_rows(const uint8_t* __restrict__ xq, const
 
 // Zero one padding row of a GEMM-aligned layout (its codes or BF16 values,
 // and its scales in FP8 mode).  Called by a whole wave.
+template <bool NT>
 __device__ __forceinline__ void zero_row(void* __restrict__ recv, float* __restrict__ scales, int row,
                                          int H, bool fp8, int scale_ld)
 {
@@ -227,7 +234,7 @@ __device__ __forceinline__ void zero_row(void* __restrict__ recv, float* __restr
     uint8_t* dst = static_cast<uint8_t*>(recv) + (size_t)row * row_bytes;
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
     for (size_t off = (size_t)lane * 16; off < row_bytes; off += kWave * 16)
-        store16_hint<EP_DISPATCH_NT_STORE>(dst + off, z);
+        store16_hint<NT>(dst + off, z);
     if (fp8) {
         const int nb = H / kQBlock;
         for (int b = lane; b < nb; b += kWave)
