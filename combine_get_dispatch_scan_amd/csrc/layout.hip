@@ -25,9 +25,11 @@
 namespace moe_ep {
 
 // Counting step of chunk c (256 tokens, one per thread of a 256-thread
-// block, one block per chunk).  LDS holds, per expert, four 64-bit masks (one per wave) of the
-// tokens that chose it; a token's rank for expert e is the number of set bits
-// before it in those masks.  Writes the pair codes and token-in-partition
+// block, one block per chunk).  LDS holds, per wave and expert, a 64-bit mask
+// of the wave's tokens that chose the expert, stored wave-major ([wave][E]) so
+// that the lanes of one OR, which mostly name different experts, hit
+// consecutive words rather than words 32 bytes apart in the same banks.  A
+// token's rank for expert e is the number of set bits before it in e's masks.  Writes the pair codes and token-in-partition
 // bytes of the chunk's tokens and row c of the per-chunk count tables.
 template <int KMAX>
 __device__ __forceinline__ void count_chunk(
@@ -70,7 +72,7 @@ __device__ __forceinline__ void count_chunk(
                     ninv++;
                 } else {
                     ids[k] = (int)e;
-                    atomicOr(&lds_bits[(int)e * kChunkWaves + wave], 1ull << lane);
+                    atomicOr(&lds_bits[wave * E + (int)e], 1ull << lane);
                     pmask |= 1ull << ((int)e / epp);
                 }
             }
@@ -90,10 +92,9 @@ __device__ __forceinline__ void count_chunk(
                 int code = -1;
                 int e = ids[k];
                 if (e >= 0) {
-                    const unsigned long long* b = &lds_bits[e * kChunkWaves];
-                    int r = __popcll(b[wave] & below);
+                    int r = __popcll(lds_bits[wave * E + e] & below);
                     for (int w = 0; w < wave; ++w)
-                        r += __popcll(b[w]);
+                        r += __popcll(lds_bits[w * E + e]);
                     code = (e << 8) | r;
                 }
                 pair_code[(size_t)t * K + k] = code;
@@ -118,7 +119,7 @@ __device__ __forceinline__ void count_chunk(
         int n = 0;
 #pragma unroll
         for (int w = 0; w < kChunkWaves; ++w)
-            n += __popcll(lds_bits[e * kChunkWaves + w]);
+            n += __popcll(lds_bits[w * E + e]);
         chunk_cnt[(size_t)c * E + e] = n;
     }
     if (tid < P)
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kChunk) void layout_chunk_kernel(
     int32_t* __restrict__ pair_code, int32_t* __restrict__ chunk_cnt,
     int32_t* __restrict__ chunk_pcnt, int32_t* __restrict__ chunk_inv)
 {
-    extern __shared__ unsigned long long lds_bits[];     // [E][kChunkWaves]
+    extern __shared__ unsigned long long lds_bits[];     // [kChunkWaves][E]
     __shared__ int lds_pcnt[64];
     __shared__ int lds_inv;
     count_chunk<KMAX>(topk_idx, T, K, E, P, blockIdx.x, is_token_in_partition, wide_mask_store,
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kChunk) void layout_single_kernel(
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_tokens_per_partition,
     int32_t* __restrict__ num_invalid, int32_t* __restrict__ status)
 {
-    extern __shared__ unsigned long long lds_bits[];     // [E][kChunkWaves]
+    extern __shared__ unsigned long long lds_bits[];     // [kChunkWaves][E]
     __shared__ int lds_pcnt[64];
     __shared__ int lds_inv;
     __shared__ int lds_wave[kChunk / kWave];
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(kChunk) void layout_single_kernel(
         if (j < epT && e < E) {
 #pragma unroll
             for (int w = 0; w < kChunkWaves; ++w)
-                n_e[j] += __popcll(lds_bits[e * kChunkWaves + w]);
+                n_e[j] += __popcll(lds_bits[w * E + e]);
             blk_e[j] = align == 1 ? n_e[j] : (n_e[j] + align - 1) / align * align;
             part += blk_e[j];
         }

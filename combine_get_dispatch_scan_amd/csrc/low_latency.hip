@@ -47,21 +47,21 @@ struct LLArgs {
     int32_t* num_invalid;
 };
 
-// Rank of token t among the tokens of expert e (bits below t in e's masks).
-__device__ __forceinline__ int rank_of(const unsigned long long* bits, int e, int t)
+// Rank of token t among the tokens of expert e (bits below t in e's masks;
+// the masks are wave-major, [kLLWaves][E]).
+__device__ __forceinline__ int rank_of(const unsigned long long* bits, int E, int e, int t)
 {
-    const unsigned long long* b = bits + e * kLLWaves;
     const int w = t / kWave;
-    int r = __popcll(b[w] & ((1ull << (t % kWave)) - 1ull));
+    int r = __popcll(bits[w * E + e] & ((1ull << (t % kWave)) - 1ull));
     for (int i = 0; i < w; ++i)
-        r += __popcll(b[i]);
+        r += __popcll(bits[i * E + e]);
     return r;
 }
 
 template <int KMAX, bool FP8>
 __global__ __launch_bounds__(kLLThreads) void low_latency_dispatch_kernel(LLArgs a)
 {
-    extern __shared__ unsigned long long lds_bits[];     // [E][kLLWaves]
+    extern __shared__ unsigned long long lds_bits[];     // [kLLWaves][E]
     __shared__ int lds_ids[kLLThreads * KMAX];           // valid expert id or -1
     __shared__ unsigned long long lds_pmask[kLLThreads]; // partitions of each token
     __shared__ int lds_pcnt[64];
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kLLThreads) void low_latency_dispatch_kernel(LLArgs
                     ninv++;
                 } else {
                     ids[k] = (int)e;
-                    atomicOr(&lds_bits[(int)e * kLLWaves + wave], 1ull << lane);
+                    atomicOr(&lds_bits[wave * E + (int)e], 1ull << lane);
                     pmask |= 1ull << ((int)e / epp);
                 }
             }
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kLLThreads) void low_latency_dispatch_kernel(LLArgs
             if (j < epT && e < E) {
 #pragma unroll
                 for (int w = 0; w < kLLWaves; ++w)
-                    n_e[j] += __popcll(lds_bits[e * kLLWaves + w]);
+                    n_e[j] += __popcll(lds_bits[w * E + e]);
                 a.num_tokens_per_expert[e] = n_e[j];
                 part += min(n_e[j], a.cap);
                 ovf |= n_e[j] > a.cap;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kLLThreads) void low_latency_dispatch_kernel(LLArgs
     if (lane < K) {
         const int e = lds_ids[t_row * KMAX + lane];
         if (e >= 0) {
-            const int r = rank_of(lds_bits, e, t_row);
+            const int r = rank_of(lds_bits, E, e, t_row);
             if (r < a.cap)
                 s_own = e * a.cap + r;
         }
