@@ -44,7 +44,7 @@ DESCR = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="v3", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
