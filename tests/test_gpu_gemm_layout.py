@@ -180,3 +180,39 @@ def test_option_validation(ep):
         ep.get_dispatch_layout(torch.from_numpy(idx).to(dev), 16, 4, expert_alignment=0)
     with pytest.raises(ep.EpError):
         ep.get_dispatch_layout(torch.from_numpy(idx).to(dev), 16, 4, expert_alignment=2048)
+
+
+def test_fp8_cached_combine_and_backward_on_aligned_and_static_handles(ep):
+    """The calls that take a handle work the same on an aligned (padded) and a
+    low-latency (static) handle: FP8 cached dispatch, FP8 combine, the backward
+    of combine (padding rows keep their contents) -- each against the oracle."""
+    dev = _dev()
+    T, H, K, E, P, A, cap = 120, 1024, 4, 16, 4, 32, 40
+    idx, w = workloads.random_case(131, T, E, K, mask_frac=0.05)
+    x = workloads.random_rows(132, T, H, "wide")
+    t_idx, t_w = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
+    handles = []
+    lay = ep.get_dispatch_layout(t_idx, E, P, expert_alignment=A)
+    recv_a, sc_a, h_a = ep.dispatch(_bf16(x, dev), t_w, lay, True)
+    handles.append(("aligned", h_a, h_a.c.capacity_rows))
+    recv_s, sc_s, lay_s = ep.low_latency_dispatch(_bf16(x, dev), t_idx, t_w, E, P, cap, True)
+    handles.append(("static", lay_s.handle, E * cap))
+    for name, h, rows in handles:
+        slot = h.slot.cpu().numpy()
+        # cached FP8 dispatch of new rows
+        x2 = workloads.random_rows(133, T, H, "normal")
+        r2, s2 = ep.dispatch_cached(_bf16(x2, dev), h)
+        ref = oracle.dispatch(x2, slot, rows, True)
+        used = slot[slot >= 0]
+        assert np.array_equal(r2.view(torch.uint8).cpu().numpy()[used], ref[0][used]), name
+        assert np.array_equal(s2.cpu().numpy()[used].view(np.uint32), ref[1][used].view(np.uint32)), name
+        # FP8 combine of those rows
+        out = ep.combine_fp8(r2, s2, h)
+        q = r2.view(torch.uint8).cpu().numpy()
+        assert np.array_equal(_bits(out), oracle.combine_fp8(q, s2.cpu().numpy(), slot, w)), name
+        # backward of combine: rows no pair maps to keep the fill
+        g = workloads.random_rows(134, T, H)
+        gy0 = torch.full((rows, H), 0x1234, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        gy, _ = ep.combine_backward(_bf16(g, dev), h, grad_y=gy0)
+        want, _ = oracle.combine_backward(g, None, slot, w, rows, fill=0x1234)
+        assert np.array_equal(_bits(gy), want), name
