@@ -158,11 +158,14 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int num_tokens, int num_topk
  *   use_fp8        0: recv_x is bf16 [capacity_rows*H]; 1: recv_x is
  *                  e4m3fn bytes [capacity_rows*H], recv_scales fp32
  *                  [capacity_rows*H/128]
- *   capacity_rows  rows in recv_x; T*K never overflows, or pass the exact N
- *                  read back by ep_handle_recv_counts.  Pairs whose row would
- *                  be >= capacity_rows are dropped (slot -1) and flagged.
+ *   capacity_rows  rows in recv_x, at most T*K (T*K + E*(A-1) for a layout
+ *                  aligned to A rows); that maximum never overflows, or pass
+ *                  the exact N read back by ep_handle_recv_counts.  Pairs
+ *                  whose row would be >= capacity_rows are dropped (slot -1)
+ *                  and flagged.
  *   handle         in: from the layout call; out: stage 2
- * Receive rows at and beyond N are not written.
+ * Receive rows at and beyond N (the end of the last expert block) are not
+ * written.
  * Errors: EP_EINVAL, EP_EHIP.  Overflow is reported by ep_handle_recv_counts.
  */
 int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp8,
@@ -182,7 +185,7 @@ int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp
  * count are not written.
  *
  *   x, topk_idx, topk_weights   as for ep_get_dispatch_layout / ep_dispatch;
- *                               1 <= num_tokens <= EP_MAX_LL_TOKENS (0 allowed)
+ *                               0 <= num_tokens <= EP_MAX_LL_TOKENS
  *   num_max_tokens              cap, rows per expert (E*cap < 2^31)
  *   recv_x                      bf16 or e4m3fn [E*cap*H]; recv_scales fp32
  *                               [E*cap*H/128] in FP8 mode
