@@ -111,7 +111,7 @@ void debug_launch(const char* kernel, dim3 grid, dim3 block, size_t lds)
 
 extern "C" {
 
-int ep_version(void) { return 10100; }
+int ep_version(void) { return EP_VERSION; }
 
 const char* ep_last_error(void) { return g_err.c_str(); }
 

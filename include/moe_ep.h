@@ -106,7 +106,9 @@ typedef struct ep_handle {
     int32_t  reserved;
 } ep_handle_t;
 
-/* Library version, major*10000 + minor*100 + patch. */
+/* Library version, major*10000 + minor*100 + patch.  EP_VERSION is the
+ * version of this header; ep_version() that of the loaded library. */
+#define EP_VERSION 10100
 int ep_version(void);
 
 /* Message describing the last error returned on this thread ("" if none). */
