@@ -321,9 +321,11 @@ int ep_dispatch_backward_fp8(const void* grad_recv, const float* grad_scales,
  *                 not written
  *   grad_w        device fp32 [T*K] or NULL.  Each dot product is reduced in
  *                 a fixed order (per-lane fma chains over the hidden
- *                 dimension, then a 64-lane tree), so results are
- *                 deterministic; against the exact sum the error is at most
- *                 about (H/64 + 8) * 2^-24 * sum_j |grad_out * y|.
+ *                 dimension, a 64-lane tree, then 8 wave partials added in
+ *                 wave order), so results are deterministic; against the
+ *                 exact sum the error is at most gamma_d * sum_j |grad_out*y|,
+ *                 gamma_d = d*2^-24/(1 - d*2^-24), d = 8*ceil(ceil(H/512)/8)
+ *                 + 13 (29 for H = 7168).
  * Errors: EP_EINVAL, EP_EHIP.
  */
 int ep_combine_backward(const void* grad_out, const void* y, const ep_handle_t* handle,

@@ -7,6 +7,7 @@ import pytest
 
 import oracle
 import workloads
+from conftest import grad_w_rel_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +62,7 @@ def test_dispatch_and_combine_gradients(ep):
             if s < 0:
                 assert gw[t, k] == 0.0
                 continue
-            tol = (H / 64 + 8) * 2.0 ** -24 * np.abs(gf[t] * yf[s]).sum() + 2.0 ** -24 * abs(want_gw[t, k])
+            tol = grad_w_rel_bound(H) * np.abs(gf[t] * yf[s]).sum() + 2.0 ** -24 * abs(want_gw[t, k])
             assert abs(gw[t, k] - want_gw[t, k]) <= tol + 1e-38
 
 

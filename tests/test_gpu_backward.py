@@ -3,13 +3,14 @@
 grad_x and grad_y are bit-exact (same fp32 operations); grad_w is an fp32
 dot product reduced in a fixed order on the GPU and in double by the oracle,
 so it is compared within the bound that order implies:
-|gpu - exact| <= (H/64 + 8) * 2^-24 * sum_j |g_j y_j|  (+ the oracle's own
+|gpu - exact| <= gamma_d * sum_j |g_j y_j| (d the reduction depth)  (+ the oracle's own
 rounding to fp32), and it must be bit-identical from run to run."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads
+from conftest import grad_w_rel_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +49,7 @@ def _check_grad_w(got, ref_exact_f32, g, y, slot, H):
                 assert got[t, k] == 0.0
                 continue
             mag = np.abs(gf[t] * yf[s]).sum()
-            tol = (H / 64 + 8) * 2.0 ** -24 * mag + 2.0 ** -24 * abs(float(ref_exact_f32[t, k])) + 1e-38
+            tol = grad_w_rel_bound(H) * mag + 2.0 ** -24 * abs(float(ref_exact_f32[t, k])) + 1e-38
             assert abs(float(got[t, k]) - float(ref_exact_f32[t, k])) <= tol, (t, k, got[t, k], ref_exact_f32[t, k])
 
 
