@@ -199,6 +199,56 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_fp8_kernel(Comb
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
 
+    if constexpr (UNIT) {
+        // Unit weights read the rows and scales through per-row buffer
+        // descriptors, with no predicated load: a masked pair's descriptors
+        // have an empty range and read zeros, as do lanes past the row end
+        // (whose stores the output descriptor drops), and its weight is 0, so
+        // fma(0, 0, acc) leaves acc (which starts at +0 and never becomes -0).
+        // The predicated form below, compiled with a constant weight, waited
+        // for each gather before issuing the next: 117.5 us against 100.3 us
+        // at 8192 x 7168 top-8.  With read weights the predicated form is the
+        // faster one (98.5 us against 101.0 us).
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            wk[k] = sk[k] >= 0 ? 1.0f : 0.0f;
+        for (int i = i_begin; i < i_end; ++i) {
+            const int cb = i * kCombineFp8ChPerIter + lane * 16;
+            u32x4 d[KMAX];
+            float sc[KMAX];
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                d[k] = buffer_load16<EP_COMBINE_NT_LOAD ? 2 : 0>(row_rsrc(a.y, sk[k], H), cb);
+                sc[k] = buffer_load_f32(row_rsrc(a.scales, sk[k], nb * 4), cb / kQBlock * 4);
+            }
+            float acc[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v[4];
+                    e4m3fn_pair_to_f32<false>(d[k][j], v[0], v[1]);
+                    e4m3fn_pair_to_f32<true>(d[k][j], v[2], v[3]);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc[4 * j + b] = __builtin_fmaf(wk[k], v[b] * sc[k], acc[4 * j + b]);
+                }
+            }
+            u32x4 o0, o1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                o0[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+                o1[j] = pack_bf16x2(acc[8 + 2 * j], acc[8 + 2 * j + 1]);
+            }
+            buffer_store16<EP_COMBINE_FP8_STORE_AUX>(o0, orow, cb * 2);
+            buffer_store16<EP_COMBINE_FP8_STORE_AUX>(o1, orow, cb * 2 + 16);
+        }
+        return;
+    }
+
     for (int i0 = i_begin; i0 < i_end; i0 += kCombineFp8Unroll) {
         u32x4 d[kCombineFp8Unroll][KMAX];
         float sc[kCombineFp8Unroll][KMAX];

@@ -86,6 +86,30 @@ __device__ __forceinline__ void buffer_store16(u32x4 v, __amdgpu_buffer_rsrc_t r
     __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, AUX);
 }
 
+// Buffer-resource loads.  Offsets at or past the descriptor's range read
+// zeros without touching memory, so a descriptor with an empty range stands
+// for a row that does not exist (a masked pair), and lanes past the row end
+// need no branch.
+template <int AUX>
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, AUX);
+}
+
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// Descriptor of row `row` (`row_bytes` bytes) of a row-major array, or an
+// empty range when row < 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int row, int row_bytes)
+{
+    const bool valid = row >= 0;
+    const char* p = static_cast<const char*>(base) + (valid ? (size_t)row * row_bytes : 0);
+    return make_rsrc(const_cast<char*>(p), valid ? row_bytes : 0);
+}
+
 // BF16 <-> fp32.  Widening is exact; narrowing rounds to nearest, ties to
 // even, on the 16 dropped bits (operands are finite by contract).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
