@@ -185,11 +185,19 @@ def measure_low_latency(config, ll_cap, steps, warmup):
     torch.cuda.synchronize()
     assert nrecv.value == N, (nrecv.value, N)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    stamps = [time.perf_counter()]
     for i in range(steps):
         step()
+        stamps.append(time.perf_counter())
     torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    ms_per_step = (time.perf_counter() - stamps[0]) * 1e3 / steps
+    # each step ends when the host holds the counts (combine still queued), so
+    # the intervals between step ends spread around the step time; a step the
+    # host reached late is followed by a short interval, so no minimum
+    per_step_us = sorted((b - a) * 1e6 for a, b in zip(stamps, stamps[1:]))
+    step_stats = {"median": round(statistics.median(per_step_us), 2),
+                  "p90": round(per_step_us[int(0.9 * (len(per_step_us) - 1))], 2),
+                  "note": "intervals between the host's step ends"}
 
     # kernel duration: back-to-back launches keep the GPU busy, so events
     # around a batch time the kernels rather than the host's launch gaps
@@ -255,6 +263,7 @@ def measure_low_latency(config, ll_cap, steps, warmup):
         "config": {"workload": DESCR[config] + ", one-launch static-capacity dispatch",
                    "tokens": T, "hidden": H, "experts": E, "topk": K, "partitions": P,
                    "dispatched_pairs": N, "rows_per_expert": cap},
+        "us_per_step_stats": step_stats,
         "graph_replay_us_per_step": round(graph_ms * 1e3, 2),
         "kernels_us": {"low_latency_dispatch": round(disp_us, 2), "combine": round(comb_us, 2)},
         "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},
@@ -375,11 +384,20 @@ def main():
     dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    stamps = [t0]
     for i in range(args.steps):
         step(dev_ev[i], dom)
+        stamps.append(time.perf_counter())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # each step ends when the host holds the counts (combine still queued), so
+    # the intervals between step ends spread around the step time; a step the
+    # host reached late is followed by a short interval, so no minimum
+    per_step_us = sorted((b - a) * 1e6 for a, b in zip(stamps, stamps[1:]))
+    step_stats = {"median": round(statistics.median(per_step_us), 2),
+                  "p90": round(per_step_us[int(0.9 * (len(per_step_us) - 1))], 2),
+                  "note": "intervals between the host's step ends"}
     dom_all = sorted(e[0].elapsed_time(e[1]) for e in dev_ev)
     dom_ms = mean(dom_all)
     dom_stats = {"median": round(dom_all[len(dom_all) // 2] * 1e3, 2), "min": round(dom_all[0] * 1e3, 2),
@@ -527,6 +545,7 @@ def main():
             "launch_us": dom_stats,
             "traffic": measured_traffic(args.config, dom_kernel),
         },
+        "step_us": step_stats,
         "phases_us": {k: round(v * 1e3, 2) for k, v in phases.items()},
         "cold_step_us": {"median": round(cold_us[len(cold_us) // 2], 2), "min": round(cold_us[0], 2),
                          "note": "each step after reading a 2 GiB scratch buffer, events around the step"},
@@ -546,9 +565,11 @@ def main():
 
     if args.config == "v3":
         # the decode-shape path through the one-launch dispatch, for reference
-        ll = measure_low_latency("decode", 0, 50, 10)
+        ll = measure_low_latency("decode", 0, 1000, 10)
         res["low_latency_decode"] = {
-            "workload": ll["config"]["workload"], "us_per_step": round(ll["ms_per_step"] * 1e3, 2),
+            "workload": ll["config"]["workload"], "steps": ll["steps"],
+            "us_per_step": round(ll["ms_per_step"] * 1e3, 2),
+            "us_per_step_stats": ll["us_per_step_stats"],
             "graph_replay_us_per_step": ll["graph_replay_us_per_step"], "kernels_us": ll["kernels_us"],
             "dispatch_roofline_frac": ll["roofline"]["frac"]}
 
