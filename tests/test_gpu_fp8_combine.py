@@ -112,6 +112,10 @@ def test_capacity_drops_and_empty(ep):
     out = ep.combine_fp8(recv, sc, h)
     ref = oracle.combine_fp8(recv.view(torch.uint8).cpu().numpy(), sc.cpu().numpy(), slot, w)
     assert np.array_equal(_bits(out), ref)
+    # dropped pairs read nothing in the unit-weight form either
+    gx = ep.dispatch_backward_fp8(recv, sc, h)
+    ref_u = oracle.combine_fp8(recv.view(torch.uint8).cpu().numpy(), sc.cpu().numpy(), slot, None)
+    assert np.array_equal(_bits(gx), ref_u)
     # T = 0: nothing to do, no error
     lay0 = ep.get_dispatch_layout(torch.empty((0, K), dtype=torch.int64, device=dev), E, 2)
     _, _, h0 = ep.dispatch(torch.empty((0, H), dtype=torch.bfloat16, device=dev), None, lay0, True)

@@ -210,6 +210,9 @@ def test_fp8_cached_combine_and_backward_on_aligned_and_static_handles(ep):
         out = ep.combine_fp8(r2, s2, h)
         q = r2.view(torch.uint8).cpu().numpy()
         assert np.array_equal(_bits(out), oracle.combine_fp8(q, s2.cpu().numpy(), slot, w)), name
+        # and its unit-weight form, the dequantising backward of dispatch
+        gx = ep.dispatch_backward_fp8(r2, s2, h)
+        assert np.array_equal(_bits(gx), oracle.combine_fp8(q, s2.cpu().numpy(), slot, None)), name
         # backward of combine: rows no pair maps to keep the fill
         g = workloads.random_rows(134, T, H)
         gy0 = torch.full((rows, H), 0x1234, dtype=torch.int16, device=dev).view(torch.bfloat16)
