@@ -29,7 +29,7 @@ namespace moe_ep {
 #define EP_COMBINE_WAVES 4
 #endif
 // Cache policy, measured on MI355X.  The gathered rows are touched once:
-// non-temporal loads (plain loads cost ~30 us more at the V3 shape).
+// non-temporal loads (plain loads: 204.6 against 170.8 us at the V3 shape).
 //
 // Output stores: at the V3 shape (117 MB of output) device-scope (sc1)
 // buffer stores, which write through the XCD's L2, are fastest: ~173 us,
@@ -161,9 +161,10 @@ struct CombineFp8Args {
 #ifndef EP_COMBINE_FP8_MAX_ITERS
 #define EP_COMBINE_FP8_MAX_ITERS 4
 #endif
-// Measured at the V3 shape (dispatch backward on dispatch's own FP8 rows):
-// plain write-back stores 122 us, write-through (sc1) 128 us; two wave steps
-// in flight per wave 133 us; plain loads of the rows 156 us.
+// Output stores, measured at the V3 shape on dispatch's own FP8 rows, for
+// the weighted / unit-weight kernels: plain write-back 99.0 / 98.4 us,
+// non-temporal 106.6 / 109.3 us, write-through (sc1) 122.7 / 122.3 us.
+// Plain loads of the rows instead of non-temporal ones: 118.2 / 118.8 us.
 #ifndef EP_COMBINE_FP8_STORE_AUX
 #define EP_COMBINE_FP8_STORE_AUX 0
 #endif
