@@ -1,0 +1,60 @@
+"""Generated-code checks (CPU: hipcc cross-compiles for gfx950, nothing runs).
+
+The combine kernels are bandwidth-bound only while each wave keeps its K row
+gathers in flight together.  With the weight fixed at 1.0, the predicated
+form of the FP8 combine once compiled to a full wait (`s_waitcnt vmcnt(0)`)
+ahead of every row load, one gather at a time per wave, and ran 20% slower.
+These tests compile the combine source with the library's own flags and
+check, in the assembly, that no 16-byte row load of the hot-path
+instantiations sits right behind such a wait.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from combine_get_dispatch_scan_amd import _build
+
+# instantiations with K <= 8 on the forward and backward paths
+KERNELS = {
+    "combine_kernel<8, weighted, sc1 stores>": "_ZN6moe_ep14combine_kernelILi8ELb0ELi16EEEvNS_11CombineArgsE",
+    "combine_kernel<8, unit, sc1 stores>": "_ZN6moe_ep14combine_kernelILi8ELb1ELi16EEEvNS_11CombineArgsE",
+    "combine_kernel<8, weighted, nt stores>": "_ZN6moe_ep14combine_kernelILi8ELb0ELi2EEEvNS_11CombineArgsE",
+    "combine_fp8_kernel<8, weighted>": "_ZN6moe_ep18combine_fp8_kernelILi8ELb0EEEvNS_14CombineFp8ArgsE",
+    "combine_fp8_kernel<8, unit>": "_ZN6moe_ep18combine_fp8_kernelILi8ELb1EEEvNS_14CombineFp8ArgsE",
+    "combine_fp8_kernel<4, unit>": "_ZN6moe_ep18combine_fp8_kernelILi4ELb1EEEvNS_14CombineFp8ArgsE",
+}
+
+ROW_LOAD = re.compile(r"^(global_load_dwordx4|buffer_load_dwordx4)\b")
+
+
+@pytest.fixture(scope="module")
+def combine_asm(tmp_path_factory):
+    if not os.path.exists(_build.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "combine.s"
+    flags = [f for f in _build.FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [_build.HIPCC, *flags, "--cuda-device-only", "-S", "-I", _build.INCLUDE, "-I", _build.CSRC,
+           os.path.join(_build.CSRC, "combine.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _body(asm, symbol):
+    start = asm.index(symbol + ":")
+    end = asm.index("s_endpgm", start)
+    lines = [l.strip() for l in asm[start:end].splitlines()]
+    return [l for l in lines if l and not l.startswith((";", "."))]
+
+
+@pytest.mark.parametrize("name", sorted(KERNELS))
+def test_row_gathers_are_not_serialised(combine_asm, name):
+    body = _body(combine_asm, KERNELS[name])
+    loads = [i for i, l in enumerate(body) if ROW_LOAD.match(l)]
+    assert len(loads) >= 4, f"{name}: expected the K row gathers in the body"
+    waited = [i for i in loads
+              if any(l.startswith("s_waitcnt vmcnt(0)") for l in body[max(0, i - 3):i])]
+    assert not waited, (f"{name}: {len(waited)} of {len(loads)} row gathers wait for all "
+                        f"earlier loads first:\n" + "\n".join(body[i] for i in waited[:4]))
