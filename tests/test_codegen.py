@@ -43,6 +43,8 @@ def combine_asm(tmp_path_factory):
 
 
 def _body(asm, symbol):
+    assert symbol + ":" in asm, (f"{symbol} is not in the compiled combine.hip: the kernel's "
+                                 "template or argument list changed; update KERNELS")
     start = asm.index(symbol + ":")
     end = asm.index("s_endpgm", start)
     lines = [l.strip() for l in asm[start:end].splitlines()]
