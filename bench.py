@@ -107,15 +107,48 @@ def measured_traffic(config, kernel):
 
 
 def cpu_baseline(wl, idx, w, x, y, runs):
-    """The oracle, single-threaded, on the full workload: one whole step per run."""
+    """The oracle, single-threaded, on the full workload: one whole step per
+    run.  Returns the median time, N, and the last run's results (every
+    intermediate plus the combine output) for the parity check."""
     import oracle
     times = []
     for _ in range(runs):
         t0 = time.perf_counter()
         r = oracle.run_all(idx, w, x, wl.E, wl.P, wl.use_fp8)
-        oracle.combine(y, r["slot"], w)
+        out = oracle.combine(y, r["slot"], w)
         times.append(time.perf_counter() - t0)
-    return statistics.median(times), r["N"]
+    r["out"] = out
+    return statistics.median(times), r["N"], r
+
+
+def bf16_ulp_distance(a, b):
+    """Largest distance in BF16 ulps between two arrays of BF16 bit patterns
+    (an order-preserving map of the patterns to integers; +0 and -0 meet)."""
+    def order(v):
+        v = v.astype(np.int64)
+        return np.where(v >= 0x8000, 0x10000 - v, v + 0x8000)
+    return int(np.abs(order(a) - order(b)).max()) if a.size else 0
+
+
+def parity_verdict(gpu, ref, N, use_fp8):
+    """Compare the last timed step's outputs with the oracle's, element by
+    element: layout, slots, received rows and scales bit for bit, combine as
+    the largest BF16 ulp distance (the bar is 1; same fma order gives 0)."""
+    eq = lambda a, b: bool(np.array_equal(a, b))
+    v = {
+        "layout": eq(gpu["ntpe"], ref["num_tokens_per_expert"]) and eq(gpu["ntpp"], ref["num_tokens_per_partition"])
+        and eq(gpu["itip"], ref["is_token_in_partition"]) and gpu["ninv"] == ref["num_invalid"],
+        "slot": eq(gpu["slot"], ref["slot"]),
+        "recv_rows": eq(gpu["recv"], ref["recv_x"][:N]),
+    }
+    if use_fp8:
+        v["recv_scales"] = eq(gpu["scales"].view(np.uint32), ref["recv_scales"][:N].view(np.uint32))
+    ulp = bf16_ulp_distance(gpu["out"], ref["out"])
+    verdict = {k: "bit-exact" if ok else "MISMATCH" for k, ok in v.items()}
+    verdict["combine_max_ulp"] = ulp
+    verdict["combine"] = "bit-exact" if ulp == 0 else ("within 1 ulp" if ulp <= 1 else "MISMATCH")
+    verdict["checked"] = "last timed step against the oracle on the full workload"
+    return verdict
 
 
 def bench_low_latency(args):
@@ -404,6 +437,20 @@ def main():
                  "p90": round(dom_all[min(len(dom_all) - 1, int(0.9 * len(dom_all)))] * 1e3, 2)}
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {dom} {dom_ms * 1e3:.2f} us",
           file=sys.stderr, flush=True)
+    # the last timed step's outputs, kept for the parity check against the
+    # oracle that the CPU-baseline leg runs on the same inputs
+    gpu_out = None
+    if not args.no_cpu_baseline:
+        slot_off = h.slot - ws.data_ptr()
+        gpu_out = {
+            "ntpe": ntpe.cpu().numpy(), "ntpp": ntpp.cpu().numpy(), "itip": itip.cpu().numpy(),
+            "ninv": int(ninv.cpu()[0]),
+            "slot": ws[slot_off:slot_off + T * K * 4].view(torch.int32).cpu().numpy().reshape(T, K),
+            "recv": (recv[:N].cpu().numpy() if wl.use_fp8
+                     else recv[:N].view(torch.int16).cpu().numpy().view(np.uint16)),
+            "scales": scales[:N].cpu().numpy() if wl.use_fp8 else None,
+            "out": out.view(torch.int16).cpu().numpy().view(np.uint16),
+        }
 
     # cold steps: reading a 2 GiB scratch buffer before each step evicts the
     # Infinity Cache (256 MB) and the L2s with clean lines (a fill would leave
@@ -575,8 +622,10 @@ def main():
 
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_runs} oracle runs)", file=sys.stderr, flush=True)
-        sec, n_cpu = cpu_baseline(wl, idx, w, x, y, args.cpu_runs)
+        sec, n_cpu, ref = cpu_baseline(wl, idx, w, x, y, args.cpu_runs)
         assert n_cpu == N
+        res["parity"] = parity_verdict(gpu_out, ref, N, wl.use_fp8)
+        print(f"[bench] parity: {res['parity']}", file=sys.stderr, flush=True)
         res["cpu_baseline"] = {
             "value": round(logical / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"whole step (layout, slots, {'FP8' if wl.use_fp8 else 'BF16'} dispatch, combine) "

@@ -4,6 +4,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -40,3 +41,47 @@ def test_bf16_byte_counts_have_no_scales():
     wl = workloads.config("skewed")
     bc = bench.byte_counts(wl, 1000)
     assert bc["dispatch_logical"] == 1000 * wl.H * 2
+
+
+def test_bf16_ulp_distance():
+    u = lambda *v: np.array(v, dtype=np.uint16)
+    assert bench.bf16_ulp_distance(u(0x3F80), u(0x3F80)) == 0
+    assert bench.bf16_ulp_distance(u(0x3F80), u(0x3F81)) == 1
+    assert bench.bf16_ulp_distance(u(0x0000), u(0x8000)) == 0       # +0 and -0 meet
+    assert bench.bf16_ulp_distance(u(0x0001), u(0x8001)) == 2       # across zero
+    assert bench.bf16_ulp_distance(u(0xBF80), u(0xBF81)) == 1
+    assert bench.bf16_ulp_distance(u(0x3F80, 0x4000), u(0x3F80, 0x4003)) == 3
+
+
+def _gpu_like(ref, N):
+    """The oracle's own results, shaped like the bench's snapshot of a step."""
+    return {"ntpe": ref["num_tokens_per_expert"].copy(), "ntpp": ref["num_tokens_per_partition"].copy(),
+            "itip": ref["is_token_in_partition"].copy(), "ninv": ref["num_invalid"],
+            "slot": ref["slot"].copy(), "recv": ref["recv_x"][:N].copy(),
+            "scales": ref["recv_scales"][:N].copy() if ref["recv_scales"] is not None else None,
+            "out": ref["out"].copy()}
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_parity_verdict_on_the_oracle_itself_and_planted_mistakes(name):
+    wl = workloads.config(name)
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    y = workloads.expert_outputs(wl, N)
+    _, n, ref = bench.cpu_baseline(wl, idx, w, x, y, 1)
+    assert n == N
+    v = bench.parity_verdict(_gpu_like(ref, N), ref, N, wl.use_fp8)
+    assert all(v[k] == "bit-exact" for k in ("layout", "slot", "recv_rows", "combine"))
+    assert v["combine_max_ulp"] == 0
+    # planted differences are reported
+    g = _gpu_like(ref, N)
+    g["slot"][0, 0] += 1
+    g["recv"][N - 1, -1] ^= 1
+    g["out"][3, 5] += 1
+    g["ntpe"][0] += 1
+    v = bench.parity_verdict(g, ref, N, wl.use_fp8)
+    assert v["slot"] == v["recv_rows"] == v["layout"] == "MISMATCH"
+    assert v["combine_max_ulp"] == 1 and v["combine"] == "within 1 ulp"
+    if wl.use_fp8:
+        g["scales"][0, 0] = np.nextafter(g["scales"][0, 0], np.float32(np.inf))
+        assert bench.parity_verdict(g, ref, N, True)["recv_scales"] == "MISMATCH"
