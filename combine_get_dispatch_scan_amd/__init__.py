@@ -249,9 +249,11 @@ def _ptr(t) -> Optional[int]:
 @dataclass
 class Handle:
     """Routing metadata of one dispatch (wraps ep_handle_t and keeps the
-    workspace it points into alive)."""
+    workspace it points into alive).  num_recv is the number of dispatched
+    pairs once handle_recv_counts has read it (None before)."""
     c: ep_handle_t
     ws: object
+    num_recv: Optional[int] = None
 
     @property
     def num_tokens(self):
@@ -482,6 +484,7 @@ def handle_recv_counts(handle: Handle):
     n = ctypes.c_int32(0)
     rc = _check(ep_handle_recv_counts(handle.c, counts, ctypes.byref(n), _stream()),
                 ok=(EP_OK, EP_ECAPACITY, EP_EIDS))
+    handle.num_recv = int(n.value)
     return list(counts), int(n.value), rc
 
 

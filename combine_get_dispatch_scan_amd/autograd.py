@@ -47,6 +47,21 @@ class _Dispatch(torch.autograd.Function):
         return _dispatch_backward(grad_recv.contiguous(), ctx.handle), None, None, None
 
 
+def _unmapped_rows_zeroed(y, handle):
+    """A gradient buffer shaped like y whose rows that no pair maps to are
+    zero (the combine backward writes the others).  In a dense layout whose
+    pair count the host has read (handle_recv_counts, which a grouped GEMM
+    needs anyway), those rows are exactly [min(N, capacity), rows); otherwise
+    every row is zeroed first."""
+    c = handle.c
+    dense = c.static_cap == 0 and c.expert_alignment <= 1
+    if not dense or handle.num_recv is None:
+        return torch.zeros_like(y)
+    grad_y = torch.empty_like(y)
+    grad_y[min(handle.num_recv, c.capacity_rows):].zero_()
+    return grad_y
+
+
 class _Combine(torch.autograd.Function):
     @staticmethod
     def forward(ctx, y, topk_weights, handle):
@@ -60,7 +75,7 @@ class _Combine(torch.autograd.Function):
     def backward(ctx, grad_out):
         y, w = ctx.saved_tensors
         want_w = w is not None and ctx.needs_input_grad[1]
-        grad_y = torch.zeros_like(y)              # rows no pair maps to: zero gradient
+        grad_y = _unmapped_rows_zeroed(y, ctx.handle)
         gy, gw = _combine_backward(grad_out.contiguous(), ctx.handle,
                                    y=y.detach() if want_w else None,
                                    topk_weights=w.detach() if w is not None else None,

@@ -86,3 +86,32 @@ def test_chain_through_an_expert(ep):
     # d(2 * recv) / d recv: doubling bf16 values is exact
     g_recv = workloads.bf16_bits_from_f32(2 * workloads.f32_from_bf16_bits(gy))
     assert np.array_equal(_bits(x.grad), oracle.dispatch_backward(g_recv, ref["slot"]))
+
+
+@pytest.mark.parametrize("read_counts", [True, False])
+def test_combine_gradient_rows_no_pair_maps_to_are_zero(ep, read_counts):
+    """With the pair count read on the host, the combine backward zeroes only
+    the rows past it; without, every row first.  Either way the rows no pair
+    maps to get a zero gradient and the others the oracle's."""
+    import combine_get_dispatch_scan_amd.autograd as A
+    dev = _dev()
+    T, H, E, K, P = 200, 256, 16, 4, 4
+    idx, w = workloads.random_case(51, T, E, K, mask_frac=0.2)
+    x_bits = workloads.random_rows(52, T, H)
+    t_w = torch.from_numpy(w).to(dev)
+    recv, handle = A.dispatch(_bf16(x_bits, dev), torch.from_numpy(idx).to(dev), t_w, E, P)
+    ref = oracle.run_all(idx, w, x_bits, E, P, False)
+    assert ref["N"] < recv.shape[0]              # masked pairs leave rows past N
+    if read_counts:
+        _, n, _ = ep.handle_recv_counts(handle)
+        assert n == ref["N"] and handle.num_recv == n
+    # rows past N hold leftovers in the allocator's memory: fill them first
+    y_bits = workloads.random_rows(53, recv.shape[0], H)
+    y = _bf16(y_bits, dev).requires_grad_(True)
+    out = A.combine(y, handle, None)
+    g_out = workloads.random_rows(54, T, H)
+    torch.empty_like(y).fill_(7.0)               # dirty the caching allocator's block
+    out.backward(_bf16(g_out, dev))
+    want_gy, _ = oracle.combine_backward(g_out, y_bits, ref["slot"], w, recv.shape[0], fill=0)
+    assert np.array_equal(_bits(y.grad), want_gy)
+    assert not _bits(y.grad)[ref["N"]:].any()
