@@ -91,6 +91,26 @@ MUTANTS = [
      "(double)oracle_bf16_to_f32(y[(size_t)r * H + j]);",
      "(double)wk;",
      [pins.test_combine_backward_grad_w_matches_finite_differences]),
+    ("dispatch backward: k loop reversed",
+     "            for (int k = 0; k < K; ++k) {\n                int32_t r = slot[(size_t)t * K + k];\n"
+     "                if (r < 0)\n                    continue;\n                acc = acc + oracle_bf16_to_f32(grad_recv",
+     "            for (int k = K - 1; k >= 0; --k) {\n                int32_t r = slot[(size_t)t * K + k];\n"
+     "                if (r < 0)\n                    continue;\n                acc = acc + oracle_bf16_to_f32(grad_recv",
+     [pins.test_dispatch_backward_exact_fp32_chain_in_k_order]),
+    ("FP8 combine: k loop reversed",
+     "            for (int k = 0; k < K; ++k) {\n                int32_t r = slot[(size_t)t * K + k];\n"
+     "                if (r < 0)\n                    continue;\n                float v = oracle_e4m3fn_to_f32",
+     "            for (int k = K - 1; k >= 0; --k) {\n                int32_t r = slot[(size_t)t * K + k];\n"
+     "                if (r < 0)\n                    continue;\n                float v = oracle_e4m3fn_to_f32",
+     [lambda: pins.test_combine_fp8_exact_fp32_chain_in_k_order(False),
+      lambda: pins.test_combine_fp8_exact_fp32_chain_in_k_order(True)]),
+    ("FP8 combine: multiply and add rounded separately",
+     "acc = fmaf(wk, v, acc);", "acc = acc + wk * v;",
+     [lambda: pins.test_combine_fp8_exact_fp32_chain_in_k_order(True)]),
+    ("combine backward: grad_w accumulated in fp32",
+     "double dot = 0.0;", "float dot = 0.0f;",
+     [pins.test_combine_backward_grad_w_is_the_exact_dot_rounded_once,
+      pins.test_combine_backward_grad_w_wide_range_within_double_bound]),
 ]
 
 

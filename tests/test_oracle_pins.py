@@ -877,3 +877,219 @@ def test_brute_force_tiny_dispatch_and_combine():
                         acc = _rn_f32(Fraction(float(w[t, k])) * Fraction(float(yf[s_, j])) + Fraction(acc))
                 want = torch.tensor([acc], dtype=torch.float32).to(torch.bfloat16).float().item()
                 assert out[t, j] == want or (out[t, j] == 0 and want == 0), (seed, t, j)
+
+
+# ----------------------------------------------------------------------------
+# exact-arithmetic pins of the backward reductions: the fp32 chain in
+# ascending k (one rounding per operation) and grad_w's single final rounding
+# ----------------------------------------------------------------------------
+
+def _decode_e4m3_exact(q):
+    """Exact values of E4M3FN codes, by torch's own decoder (fp32 is exact
+    for every finite code)."""
+    return torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _bf16_of(values_f64):
+    """torch's BF16 rounding (RNE) of fp32 values, as bit patterns."""
+    t = torch.from_numpy(np.asarray(values_f64, np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _wide_rows(rng, rows, H):
+    """BF16 rows whose values span many binades within and across rows, so
+    that the order of an fp32 sum changes its rounding."""
+    v = rng.standard_normal((rows, H)).astype(np.float32)
+    v *= np.ldexp(np.float32(1.0), rng.integers(-12, 13, (rows, H))).astype(np.float32)
+    return workloads.bf16_bits_from_f32(v)
+
+
+def _cancelling_pattern(slot):
+    """Per token, the roles of its dispatched pairs in ascending k: the first
+    is small, the next two are a large value and its exact negative, the rest
+    small.  Summed left to right the first small term is absorbed by the large
+    one and the cancellation leaves the later ones; summed in any other order
+    different small terms survive, which stays visible after BF16 rounding."""
+    roles = {}
+    for t in range(slot.shape[0]):
+        ks = [k for k in range(slot.shape[1]) if slot[t, k] >= 0]
+        for i, k in enumerate(ks):
+            roles[(t, k)] = ("big+" if i == 1 else "big-" if i == 2 else "small") if len(ks) >= 3 else "small"
+    return roles
+
+
+def test_dispatch_backward_exact_fp32_chain_in_k_order():
+    """grad_x[t][j] = bf16( ((0 + g_k0) + g_k1) + ... ) over the dispatched k
+    in ascending order, each addition one fp32 rounding of the exact rational
+    sum (stakiran "DeepEP 要約" section 3: the backward of dispatch is combine,
+    whose accumulation runs over k ascending).  The rows hold a small term, a
+    large value and its negative, so a reversed or reassociated sum gives a
+    different BF16 result."""
+    from fractions import Fraction
+    rng = np.random.default_rng(505)
+    H = 128
+    differs = 0
+    for case in range(12):
+        T, E, K = int(rng.integers(3, 7)), 8, int(rng.integers(3, 6))
+        idx = rng.integers(-1, E, (T, K)).astype(np.int64)
+        idx[0] = np.arange(K) % E                            # one token with K pairs
+        r = oracle.run_all(idx, np.ones((T, K), np.float32), None, E, 2, False)
+        rows = max(r["rows"], 1)
+        gv = rng.standard_normal((rows, H)).astype(np.float32)
+        for (t, k), role in _cancelling_pattern(r["slot"]).items():
+            if role == "big+":
+                big = rng.integers(128, 256, H).astype(np.float32) * np.ldexp(
+                    np.float32(1), rng.integers(20, 28, H)).astype(np.float32)
+                big *= np.where(rng.integers(0, 2, H) == 1, np.float32(-1), np.float32(1))
+                gv[r["slot"][t, k]] = big
+                k2 = [kk for kk in range(K) if r["slot"][t, kk] >= 0][2]
+                gv[r["slot"][t, k2]] = -big
+        g = workloads.bf16_bits_from_f32(gv)
+        gf = _f32(g)
+        got = oracle.dispatch_backward(g, r["slot"])
+        want = np.zeros((T, H))
+        rev = np.zeros((T, H))
+        for t in range(T):
+            ks = [k for k in range(K) if r["slot"][t, k] >= 0]
+            for j in range(H):
+                acc = 0.0
+                for k in ks:
+                    acc = _rn_f32(Fraction(acc) + Fraction(float(gf[r["slot"][t, k], j])))
+                want[t, j] = acc
+                acc = 0.0
+                for k in reversed(ks):
+                    acc = _rn_f32(Fraction(acc) + Fraction(float(gf[r["slot"][t, k], j])))
+                rev[t, j] = acc
+        assert np.array_equal(got, _bf16_of(want)), case
+        differs += int((_bf16_of(rev) != _bf16_of(want)).sum())
+    assert differs > 500        # the data tell the two orders apart after rounding
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_combine_fp8_exact_fp32_chain_in_k_order(weighted):
+    """FP8 combine: v = fp32(decode(q) * scale) (one rounding), then
+    acc = fp32(w * v + acc) per dispatched k in ascending order (one rounding
+    per fused multiply-add; w = 1 gives fp32(v + acc)), then BF16 RNE
+    (stakiran section 3: the backward of dispatch is combine; aikraft.ru
+    "Технические детали и требования": FP8 rows).  Scales are not powers of
+    two, weights are arbitrary fp32 (equal on the cancelling pair), and each
+    token's rows hold a small term, a large row and its negative: the order,
+    the fusion and the scale product all show in the BF16 result."""
+    from fractions import Fraction
+    rng = np.random.default_rng(606 + weighted)
+    H = 128
+    differs = 0
+    for case in range(10):
+        T, E, K = int(rng.integers(3, 7)), 8, int(rng.integers(3, 6))
+        idx = rng.integers(-1, E, (T, K)).astype(np.int64)
+        idx[0] = np.arange(K) % E
+        w = (rng.random((T, K)) * 2.0 - 0.5).astype(np.float32)
+        r = oracle.run_all(idx, w, None, E, 2, False)
+        rows = max(r["rows"], 1)
+        q = _finite_codes(rng, (rows, H))
+        sc = (rng.random((rows, 1)) + 0.5).astype(np.float32) * \
+            np.ldexp(np.float32(1), rng.integers(-8, 0, (rows, 1))).astype(np.float32)
+        for (t, k), role in _cancelling_pattern(r["slot"]).items():
+            if role == "big+":
+                k2 = [kk for kk in range(K) if r["slot"][t, kk] >= 0][2]
+                s1, s2 = r["slot"][t, k], r["slot"][t, k2]
+                q[s1] = (rng.integers(0x70, 0x7F, H) | (rng.integers(0, 2, H) << 7)).astype(np.uint8)
+                q[s2] = q[s1] ^ np.uint8(0x80)
+                sc[s1] = sc[s2] = np.float32(rng.random() + 0.5) * np.float32(2.0 ** 20)
+                w[t, k2] = w[t, k]
+        dec = _decode_e4m3_exact(q)
+        got = oracle.combine_fp8(q, sc, r["slot"], w if weighted else None)
+        want = np.zeros((T, H))
+        rev = np.zeros((T, H))
+        for t in range(T):
+            ks = [k for k in range(K) if r["slot"][t, k] >= 0]
+            for j in range(H):
+                terms = []
+                for k in ks:
+                    s = r["slot"][t, k]
+                    v = _rn_f32(Fraction(float(dec[s, j])) * Fraction(float(sc[s, 0])))
+                    terms.append((Fraction(float(w[t, k])) if weighted else Fraction(1), Fraction(v)))
+                acc = 0.0
+                for wk, v in terms:
+                    acc = _rn_f32(wk * v + Fraction(acc))
+                want[t, j] = acc
+                acc = 0.0
+                for wk, v in reversed(terms):
+                    acc = _rn_f32(wk * v + Fraction(acc))
+                rev[t, j] = acc
+        assert np.array_equal(got, _bf16_of(want)), case
+        differs += int((_bf16_of(rev) != _bf16_of(want)).sum())
+    assert differs > 500
+
+
+def _exact_dot_rounded_once(g_f32, y_f32):
+    """The exact dot product of two fp32 vectors (Fraction), rounded once to
+    fp32, ties to even."""
+    from fractions import Fraction
+    s = Fraction(0)
+    for a, b in zip(g_f32.tolist(), y_f32.tolist()):
+        s += Fraction(a) * Fraction(b)
+    return _rn_f32(s)
+
+
+def test_combine_backward_grad_w_is_the_exact_dot_rounded_once():
+    """grad_w[t,k] = <grad_out[t], y[slot]>: the exact sum of the H exact
+    products, rounded once to fp32 (linearity of combine in w, stakiran
+    section 3).  Values are BF16 with exponents in [-4, 4], so every partial
+    sum needs at most 40 bits: a double accumulation is exact and the result
+    must equal the rounded exact sum, while an fp32 accumulation loses bits
+    on almost every dot product."""
+    rng = np.random.default_rng(707)
+    T, E, K, H = 12, 8, 4, 256
+    idx, w = workloads.random_case(70, T, E, K, mask_frac=0.1)
+    r = oracle.run_all(idx, w, None, E, 2, False)
+
+    def rows(n):
+        m = rng.integers(128, 256, (n, H)).astype(np.float32) / np.float32(128)   # 8-bit significand
+        e = np.ldexp(np.float32(1), rng.integers(-4, 5, (n, H))).astype(np.float32)
+        sgn = np.where(rng.integers(0, 2, (n, H)) == 1, np.float32(-1), np.float32(1))
+        return workloads.bf16_bits_from_f32(m * e * sgn)
+    y = rows(r["rows"])
+    g = rows(T)
+    _, gw = oracle.combine_backward(g, y, r["slot"], w, r["rows"])
+    gf, yf = _f32(g), _f32(y)
+    f32_chain_differs = 0
+    for t in range(T):
+        for k in range(K):
+            s = r["slot"][t, k]
+            if s < 0:
+                assert gw[t, k] == 0.0
+                continue
+            want = _exact_dot_rounded_once(gf[t], yf[s])
+            assert gw[t, k] == np.float32(want), (t, k, gw[t, k], want)
+            acc = np.float32(0)
+            for a, b in zip(gf[t], yf[s]):
+                acc = np.float32(acc + np.float32(a * b))
+            f32_chain_differs += int(acc != np.float32(want))
+    assert f32_chain_differs > 10
+
+
+def test_combine_backward_grad_w_wide_range_within_double_bound():
+    """On wide-range values the double accumulation is no longer exact, but
+    its error is at most (H-1) * 2^-53 * sum|g*y| before the final rounding:
+    grad_w stays within half an fp32 ulp of the exact sum plus that, a bound
+    some 2^29 times tighter than an fp32 accumulation allows."""
+    from fractions import Fraction
+    rng = np.random.default_rng(808)
+    T, E, K, H = 10, 8, 3, 512
+    idx, w = workloads.random_case(80, T, E, K)
+    r = oracle.run_all(idx, w, None, E, 2, False)
+    y = _wide_rows(rng, r["rows"], H)
+    g = _wide_rows(rng, T, H)
+    _, gw = oracle.combine_backward(g, y, r["slot"], w, r["rows"])
+    gf, yf = _f32(g).astype(np.float64), _f32(y).astype(np.float64)
+    for t in range(T):
+        for k in range(K):
+            s = r["slot"][t, k]
+            exact = sum((Fraction(a) * Fraction(b) for a, b in zip(gf[t].tolist(), yf[s].tolist())),
+                        Fraction(0))
+            mag = float(np.abs(gf[t] * yf[s]).sum())
+            rn = _rn_f32(exact)
+            ulp = float(np.spacing(np.float32(abs(rn)))) if rn != 0 else 2.0 ** -149
+            bound = 0.5 * ulp + (H - 1) * 2.0 ** -53 * mag
+            assert abs(Fraction(float(gw[t, k])) - exact) <= Fraction(bound), (t, k)
