@@ -69,7 +69,7 @@ class ep_handle_t(ctypes.Structure):
         ("expert_alignment", ctypes.c_int32),
         ("scale_ld", ctypes.c_int32),
         ("fp8_input", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("dispatch_seq", ctypes.c_int32),
     ]
 
 

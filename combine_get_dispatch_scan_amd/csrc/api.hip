@@ -266,6 +266,7 @@ static int run_dispatch(const ep_handle_t* h, const void* x, const float* w_in, 
     L.E = h->num_experts;
     L.use_fp8 = h->use_fp8;
     L.fresh = fresh;
+    L.seq = h->dispatch_seq;
     L.capacity = h->capacity_rows;
     L.pair_code = h->pair_code;
     L.chunk_base = h->chunk_base;
@@ -316,6 +317,13 @@ int ep_dispatch_ex(const void* x, const float* x_scales, const float* topk_weigh
     h.has_weights = topk_weights != nullptr;
     h.scale_ld = scale_ld;
     h.fp8_input = x_scales != nullptr;
+    // this dispatch's number: its kernel writes it into the overflow word, so
+    // a mark left by an earlier dispatch of the same handle is not read as
+    // this one's (no clearing store is needed, the path stays capturable)
+    h.dispatch_seq = handle->stage >= 2 && handle->dispatch_seq > 0 &&
+                             handle->dispatch_seq < 0x7FFFFFFF
+                         ? handle->dispatch_seq + 1
+                         : 1;
     rc = run_dispatch(&h, x, topk_weights, recv_x, recv_scales, true, stream, x_scales);
     if (rc)
         return rc;
@@ -413,6 +421,7 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
     h.use_fp8 = use_fp8;
     h.capacity_rows = E * cap;
     h.has_weights = topk_weights != nullptr;
+    h.dispatch_seq = 1;         // the kernel writes 1 or 0 into the overflow word
     *handle = h;
     return EP_OK;
 }
@@ -501,8 +510,8 @@ static int run_combine_fp8(const void* y, const float* y_scales, const ep_handle
         return fail(EP_EINVAL, "the FP8 rows must be a non-NULL 16-byte aligned device pointer");
     if (T > 0 && handle->capacity_rows > 0 && (!y_scales || !aligned(y_scales, 4)))
         return fail(EP_EINVAL, "the FP8 scales must be a non-NULL 4-byte aligned device pointer");
-    hipError_t e = moe_ep::launch_combine_fp8(y, y_scales, T, H, handle->num_topk, handle->slot, w,
-                                              out, stream);
+    hipError_t e = moe_ep::launch_combine_fp8(y, y_scales, handle->scale_ld, T, H, handle->num_topk,
+                                              handle->slot, w, out, stream);
     if (e != hipSuccess)
         return hip_fail(e, what);
     return EP_OK;
@@ -602,10 +611,12 @@ int ep_recv_counts_decode(const ep_handle_t* handle, const int32_t* host_buf,
             host_counts[i] = off[i + 1] - off[i];
     if (host_num_recv)
         *host_num_recv = off[E];
-    // a dense layout drops pairs exactly when N exceeds the capacity, which
-    // also covers a copy taken before dispatch set the drop flag
+    // the overflow word counts only when it holds this handle's latest
+    // dispatch number; a dense layout drops pairs exactly when N exceeds the
+    // capacity, which also covers a copy taken before dispatch marked it
     const bool dense = !handle->static_cap && handle->expert_alignment <= 1;
-    if (handle->stage >= 2 && (st[0] || (dense && off[E] > handle->capacity_rows)))
+    const bool marked = st[0] != 0 && st[0] == handle->dispatch_seq;
+    if (handle->stage >= 2 && (marked || (dense && off[E] > handle->capacity_rows)))
         return fail(EP_ECAPACITY, "dispatch dropped pairs: they did not fit capacity_rows=%d",
                     handle->capacity_rows);
     if (st[1] > 0)

@@ -144,10 +144,13 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
 // decode(q) * (its block's scale), one fp32 multiply, then reduced as above.
 // Each lane owns 16 channels (one 16-byte load per row) per wave step of 1024
 // channels; its 8-lane group shares one 128-channel block, so one scale per
-// row; the 16 BF16 results leave as two 16-byte stores.
+// row; the 16 BF16 results leave as two 16-byte stores.  The scales are laid
+// out as dispatch wrote them: row-major [rows][H/128], or column-major
+// [H/128][scale_ld] (scale_ld != 0).
 struct CombineFp8Args {
     const uint8_t* y;
     const float* scales;
+    int scale_ld;
     int T, H, K;
     int nseg, iters_per_seg, iters;
     const int32_t* slot;
@@ -171,7 +174,9 @@ struct CombineFp8Args {
 constexpr int kCombineFp8ChPerIter = kWave * 16;   // 1024 channels per wave step
 constexpr int kCombineFp8Unroll = EP_COMBINE_FP8_UNROLL;
 
-template <int KMAX, bool UNIT>
+// UNIT: unit weights.  ROWBUF: unit weights on row-major scales, read through
+// per-row buffer descriptors (the hot form of the backward of dispatch).
+template <int KMAX, bool UNIT, bool ROWBUF>
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_fp8_kernel(CombineFp8Args a)
 {
     const int wi = blockIdx.x * kCombineWaves + threadIdx.x / kWave;
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_fp8_kernel(Comb
     const int i_begin = seg * a.iters_per_seg;
     const int i_end = min(a.iters, i_begin + a.iters_per_seg);
 
-    if constexpr (UNIT) {
+    if constexpr (ROWBUF) {
         // Unit weights read the rows and scales through per-row buffer
         // descriptors, with no predicated load: a masked pair's descriptors
         // have an empty range and read zeros, as do lanes past the row end
@@ -261,7 +266,8 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_fp8_kernel(Comb
             for (int k = 0; k < KMAX; ++k) {
                 if (sk[k] >= 0 && active) {
                     d[u][k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk[k] * H + cb);
-                    sc[u][k] = a.scales[(size_t)sk[k] * nb + cb / kQBlock];
+                    sc[u][k] = a.scales[a.scale_ld ? (size_t)(cb / kQBlock) * a.scale_ld + sk[k]
+                                                   : (size_t)sk[k] * nb + cb / kQBlock];
                 }
             }
         }
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_fp8_kernel(Comb
     }
 }
 
-hipError_t launch_combine_fp8(const void* y, const float* scales, int T, int H, int K,
+hipError_t launch_combine_fp8(const void* y, const float* scales, int scale_ld, int T, int H, int K,
                               const int32_t* slot, const float* w, void* out, hipStream_t stream)
 {
     if (T == 0)
@@ -309,6 +315,7 @@ hipError_t launch_combine_fp8(const void* y, const float* scales, int T, int H, 
     CombineFp8Args a;
     a.y = static_cast<const uint8_t*>(y);
     a.scales = scales;
+    a.scale_ld = scale_ld;
     a.T = T;
     a.H = H;
     a.K = K;
@@ -322,11 +329,14 @@ hipError_t launch_combine_fp8(const void* y, const float* scales, int T, int H, 
     const long long items = (long long)T * a.nseg;
     dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
     dim3 block(kCombineWaves * kWave);
-#define EP_COMBINE8(KM)                                                                          \
-    do {                                                                                         \
-        debug_launch("combine_fp8_kernel", grid, block, 0);                                      \
-        if (w) hipLaunchKernelGGL((combine_fp8_kernel<KM, false>), grid, block, 0, stream, a);   \
-        else hipLaunchKernelGGL((combine_fp8_kernel<KM, true>), grid, block, 0, stream, a);      \
+    // column-major scales with unit weights take the predicated form: a
+    // buffer descriptor cannot follow a strided column per row
+#define EP_COMBINE8(KM)                                                                                \
+    do {                                                                                               \
+        debug_launch("combine_fp8_kernel", grid, block, 0);                                            \
+        if (w) hipLaunchKernelGGL((combine_fp8_kernel<KM, false, false>), grid, block, 0, stream, a);  \
+        else if (scale_ld) hipLaunchKernelGGL((combine_fp8_kernel<KM, true, false>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((combine_fp8_kernel<KM, true, true>), grid, block, 0, stream, a);      \
     } while (0)
     if (K <= 2) EP_COMBINE8(2);
     else if (K <= 4) EP_COMBINE8(4);

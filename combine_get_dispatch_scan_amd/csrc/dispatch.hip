@@ -29,6 +29,7 @@ struct DispatchArgs {
     int row_blocks;           // workgroups that move rows; the rest zero padding
     int align;                // rows per GEMM tile of an aligned layout (1: dense)
     int scale_ld;             // 0: row-major scales, else column-major leading dim
+    int seq;                  // the handle's dispatch number (the overflow mark)
     int capacity;
     const int32_t* pair_code;
     const int32_t* chunk_base;
@@ -68,7 +69,7 @@ __device__ __forceinline__ int pair_slot(const DispatchArgs& a, int t, int seg)
                 if (a.w_in)
                     a.w_copy[i] = a.w_in[i];
                 if (ovf)
-                    a.status[0] = 1;
+                    a.status[0] = a.seq;
             }
         } else {
             s = a.slot[i];
@@ -195,6 +196,7 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
     a.B = (L.T + kChunk - 1) / kChunk;
     a.align = L.align;
     a.scale_ld = L.scale_ld;
+    a.seq = L.seq;
     a.capacity = L.capacity;
     a.pair_code = L.pair_code;
     a.chunk_base = L.chunk_base;

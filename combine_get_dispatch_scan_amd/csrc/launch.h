@@ -24,6 +24,7 @@ struct DispatchLaunch {
     int T, H, K, E;
     int use_fp8;
     bool fresh;               // compute slots from pair codes (else reuse slot[])
+    int seq;                  // the handle's dispatch number, written on overflow
     int capacity;
     int align;                // GEMM row tile of the expert blocks (1: dense)
     int scale_ld;             // 0: row-major scales, else column-major leading dimension
@@ -69,8 +70,9 @@ hipError_t launch_low_latency_dispatch(const LowLatencyLaunch& L, hipStream_t st
 hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
                           const float* w, void* out, hipStream_t stream);
 
-// combine of FP8 rows with fp32 block scales (w == nullptr: unit weights).
-hipError_t launch_combine_fp8(const void* y, const float* scales, int T, int H, int K,
+// combine of FP8 rows with fp32 block scales (w == nullptr: unit weights);
+// scale_ld 0: row-major scales, else column-major with that leading dimension.
+hipError_t launch_combine_fp8(const void* y, const float* scales, int scale_ld, int T, int H, int K,
                               const int32_t* slot, const float* w, void* out, hipStream_t stream);
 
 // backward of combine: grad_y rows (and grad_w when y != nullptr).

@@ -103,7 +103,11 @@ typedef struct ep_handle {
     int32_t  scale_ld;         /* 0: row-major scales; else column-major, this
                                   leading dimension (set by ep_dispatch_ex)      */
     int32_t  fp8_input;        /* 1 when ep_dispatch_ex got pre-quantised input    */
-    int32_t  reserved;
+    int32_t  dispatch_seq;     /* number of the handle's latest ep_dispatch /
+                                  ep_dispatch_ex (1, 2, ...): that dispatch
+                                  marks dropped pairs by writing it into the
+                                  overflow word, so an earlier dispatch's mark
+                                  is not mistaken for its own               */
 } ep_handle_t;
 
 /* Library version, major*10000 + minor*100 + patch.  EP_VERSION is the
@@ -165,10 +169,18 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int num_tokens, int num_topk
  *                  the exact N read back by ep_handle_recv_counts.  Pairs
  *                  whose row would be >= capacity_rows are dropped (slot -1)
  *                  and flagged.
- *   handle         in: from the layout call; out: stage 2
+ *   handle         in: from the layout call, or already dispatched (a
+ *                  dispatch again on the same routing, e.g. with a larger
+ *                  capacity after EP_ECAPACITY); out: stage 2.  Each dispatch
+ *                  recomputes every slot; the overflow status that
+ *                  ep_handle_recv_counts reports is the latest dispatch's.
  * Receive rows at and beyond N (the end of the last expert block) are not
  * written.
  * Errors: EP_EINVAL, EP_EHIP.  Overflow is reported by ep_handle_recv_counts.
+ *
+ * The call takes the handle the layout call filled, not topk_idx and the
+ * dimensions again: the handle already holds the routing (as per-pair codes
+ * the layout computed), the dimensions and the workspace.
  */
 int ep_dispatch(const void* x, const float* topk_weights, int hidden, int use_fp8,
                 void* recv_x, float* recv_scales, int capacity_rows,
@@ -297,7 +309,10 @@ int ep_dispatch_backward(const void* grad_recv, const ep_handle_t* handle, void*
  * decode(q) * scale (one fp32 multiply) and then reduced as in ep_combine
  * (weighted) or ep_dispatch_backward (unit weights).
  *   y / grad_recv          device e4m3fn [capacity_rows*H], receive order
- *   y_scales / grad_scales device fp32 [capacity_rows*H/128]
+ *   y_scales / grad_scales device fp32, laid out as the handle's dispatch
+ *                          wrote recv_scales: row-major [capacity_rows][H/128],
+ *                          or column-major [H/128][scale_ld] when
+ *                          ep_dispatch_ex was given scale_ld
  *   topk_weights           as for ep_combine
  *   out / grad_x           device bf16 [T*H]
  * Needs hidden % 128 == 0.  Errors: EP_EINVAL, EP_EHIP.

@@ -171,6 +171,7 @@ def test_recv_counts_decode_on_host():
     E = 6
     h = _fake_handle(stage=2, E=E, P=3)
     h.capacity_rows = 9
+    h.dispatch_seq = 1
     off = [0, 3, 4, 5, 7, 7, 9]
     for status, want in [([0, 0, 9, 0], ep.EP_OK), ([1, 0, 9, 0], ep.EP_ECAPACITY),
                          ([0, 2, 9, 0], ep.EP_EIDS), ([1, 2, 9, 0], ep.EP_ECAPACITY)]:
@@ -190,6 +191,18 @@ def test_recv_counts_decode_on_host():
     h.expert_alignment = 1
     h.static_cap = 3
     assert ep.ep_recv_counts_decode(h, buf, None, None) == ep.EP_OK
+    # the overflow word counts only when it holds the handle's latest
+    # dispatch number: a mark left by dispatch 1 is stale once dispatch 2 ran
+    h.static_cap = 0
+    h.capacity_rows = 9
+    h.dispatch_seq = 2
+    for mark, want in [(1, ep.EP_OK), (2, ep.EP_ECAPACITY), (3, ep.EP_OK)]:
+        buf = (ctypes.c_int32 * (E + 5))(*(off + [mark, 0, 9, 0]))
+        assert ep.ep_recv_counts_decode(h, buf, None, None) == want, mark
+    h.expert_alignment = 4
+    buf = (ctypes.c_int32 * (E + 5))(*(off + [1, 0, 9, 0]))
+    assert ep.ep_recv_counts_decode(h, buf, None, None) == ep.EP_OK
+    h.expert_alignment = 1
     # before dispatch the overflow word is not consulted
     h1 = _fake_handle(stage=1, E=E, P=3)
     buf = (ctypes.c_int32 * (E + 5))(*(off + [1, 0, 9, 0]))

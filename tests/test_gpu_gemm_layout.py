@@ -219,3 +219,47 @@ def test_fp8_cached_combine_and_backward_on_aligned_and_static_handles(ep):
         gy, _ = ep.combine_backward(_bf16(g, dev), h, grad_y=gy0)
         want, _ = oracle.combine_backward(g, None, slot, w, rows, fill=0x1234)
         assert np.array_equal(_bits(gy), want), name
+
+
+@pytest.mark.parametrize("A,extra_ld", [(1, 0), (16, 8)])
+def test_fp8_combine_on_column_major_scales(ep, A, extra_ld):
+    """FP8 combine and the dequantising backward of dispatch read the scales
+    in the layout the handle's dispatch wrote them: column-major [H/128][ld]
+    here (ld past the capacity when extra_ld > 0).  Checked on dispatch's own
+    rows, on a cached dispatch of new rows, and on random codes with random
+    scales, each against the oracle on the same scales transposed to rows."""
+    dev = _dev()
+    T, H, K, E, P = 150, 2048, 6, 32, 8
+    idx, w = workloads.random_case(141 + A, T, E, K, mask_frac=0.05)
+    x = workloads.random_rows(142, T, H, "wide")
+    t_idx, t_w = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
+    lay = ep.get_dispatch_layout(t_idx, E, P, expert_alignment=A)
+    h = lay.handle
+    cap = T * K + E * (A - 1)
+    ld = (cap + 3) // 4 * 4 + extra_ld
+    nb = H // 128
+    recv = torch.empty((cap, H), dtype=torch.uint8, device=dev)
+    sc = torch.full((nb, ld), -7.0, dtype=torch.float32, device=dev)
+    rc = ep.ep_dispatch_ex(_bf16(x, dev).data_ptr(), None, t_w.data_ptr(), H, 1, ld, recv.data_ptr(),
+                           sc.data_ptr(), cap, h.c, ep._stream())
+    assert rc == ep.EP_OK, ep.ep_last_error()
+    assert h.c.scale_ld == ld
+    slot = h.slot.cpu().numpy()
+    rng = np.random.default_rng(143)
+    q_rand = rng.integers(0, 256, (cap, H), dtype=np.uint32).astype(np.uint8)
+    q_rand[(q_rand & 0x7F) == 0x7F] ^= 0x01
+    s_rand = (rng.standard_normal((nb, ld)).astype(np.float32) *
+              np.ldexp(np.float32(1), rng.integers(-20, 21, (nb, ld))).astype(np.float32))
+    x2 = workloads.random_rows(144, T, H, "normal")
+    r2, s2 = ep.dispatch_cached(_bf16(x2, dev), h)
+    assert s2.shape == (nb, ld)
+    cases = [("dispatch rows", recv, sc), ("cached rows", r2, s2),
+             ("random codes", torch.from_numpy(q_rand).to(dev), torch.from_numpy(s_rand).to(dev))]
+    for name, q_t, s_t in cases:
+        print(f"[gemm] fp8 combine column-major A={A} ld={ld} {name}", flush=True)
+        out = ep.combine_fp8(q_t, s_t, h)
+        gx = ep.dispatch_backward_fp8(q_t, s_t, h)
+        q = q_t.view(torch.uint8).cpu().numpy()
+        s_rows = np.ascontiguousarray(s_t.cpu().numpy()[:, :cap].T)     # [cap][H/128]
+        assert np.array_equal(_bits(out), oracle.combine_fp8(q, s_rows, slot, w)), name
+        assert np.array_equal(_bits(gx), oracle.combine_fp8(q, s_rows, slot, None)), name

@@ -327,12 +327,14 @@ def test_counts_copied_before_dispatch_on_a_side_stream(ep):
 
 
 def test_determinism(ep):
+    """Ten runs of the whole path give bit-identical outputs (slots come
+    from integer adds over LDS masks, never from the order of atomics)."""
     wl = workloads.config("skewed")
     idx, w, x = workloads.make(wl)
     N = int((idx >= 0).sum())
     y = workloads.expert_outputs(wl, N)
     first = run_gpu(ep, idx, w, x, y, wl.E, wl.P, wl.use_fp8)
-    for _ in range(3):
+    for _ in range(9):
         again = run_gpu(ep, idx, w, x, y, wl.E, wl.P, wl.use_fp8)
         assert again["N"] == first["N"] == N
         # src_token rows at and beyond N are never written (workspace contents)
@@ -478,3 +480,94 @@ def test_two_host_threads_on_two_streams(ep):
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads)
     assert not errors, errors
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_redispatch_on_the_same_handle(ep, fp8):
+    """A dispatch that dropped pairs, then a dispatch with room for all of
+    them on the same handle (no new layout), then a short one again: each
+    reports its own overflow status and matches the oracle at its capacity
+    (the handle carries the routing, GeekNews usage section)."""
+    dev = _dev()
+    T, H, E, K, P = 257, 1024, 32, 4, 4
+    idx, w = workloads.random_case(71, T, E, K, mask_frac=0.05)
+    x = workloads.random_rows(72, T, H, "normal")
+    N = int((idx >= 0).sum())
+    lay = ep.get_dispatch_layout(torch.from_numpy(idx).to(dev), E, P)
+    t_x, t_w = _bf16_tensor(x, dev), torch.from_numpy(w).to(dev)
+    for cap in (N - 7, T * K, N - 1, N):
+        print(f"[parity] re-dispatch fp8={fp8} cap={cap} N={N}", flush=True)
+        recv, sc, h = ep.dispatch(t_x, t_w, lay, fp8, capacity_rows=cap)
+        counts, n, st = ep.handle_recv_counts(h)
+        buf = torch.full((E + 5,), -9, dtype=torch.int32, pin_memory=True)
+        ep.handle_recv_counts_async(h, buf)
+        torch.cuda.synchronize()
+        assert ep.recv_counts_decode(h, buf) == (counts, n, st)
+        ref = oracle.run_all(idx, w, x, E, P, fp8, capacity=cap)
+        assert st == (ep.EP_ECAPACITY if ref["overflow"] else ep.EP_OK), (cap, st)
+        assert n == N and np.array_equal(np.array(counts), ref["num_tokens_per_expert"])
+        assert np.array_equal(h.slot.cpu().numpy(), ref["slot"])
+        rows = ref["rows"]
+        assert np.array_equal(h.src_token.cpu().numpy()[:rows], ref["src_token"])
+        got = recv[:rows].view(torch.uint8 if fp8 else torch.int16).cpu().numpy()
+        assert np.array_equal(got if fp8 else got.view(np.uint16), ref["recv_x"])
+        if fp8:
+            assert np.array_equal(sc[:rows].cpu().numpy().view(np.uint32), ref["recv_scales"].view(np.uint32))
+        y = workloads.random_rows(73, max(rows, 1), H, "normal")
+        out = ep.combine(_bf16_tensor(y, dev), h)
+        assert np.array_equal(_bits(out), oracle.combine(y[:rows], ref["slot"], w))
+    assert h.c.dispatch_seq == 4
+
+
+def test_no_writes_past_any_output(ep):
+    """Canary bytes after the end of every layout output, and in the gaps of
+    the workspace after the handle's arrays (pair codes, slots, source tokens,
+    weight copy), stay untouched through layout, dispatch and combine."""
+    dev = _dev()
+    T, H, E, K, P = 333, 512, 24, 3, 6          # T*K = 999: arrays end inside a 256-byte region
+    idx, w = workloads.random_case(81, T, E, K, mask_frac=0.1, invalid_frac=0.02, dup_frac=0.05,
+                                   distinct=False)
+    x = workloads.random_rows(82, T, H, "normal")
+    G = 13
+    itip = torch.full((T * P + G,), 0xC3, dtype=torch.uint8, device=dev)
+    ntpp = torch.full((P + G,), -123, dtype=torch.int32, device=dev)
+    ntpe = torch.full((E + G,), -123, dtype=torch.int32, device=dev)
+    ninv = torch.full((1 + G,), -123, dtype=torch.int32, device=dev)
+    nbytes = ep.ep_workspace_bytes(T, K, E, P)
+    ws = torch.full((nbytes,), 0xE7, dtype=torch.uint8, device=dev)
+    h = ep.ep_handle_t()
+    rc = ep.ep_get_dispatch_layout(torch.from_numpy(idx).to(dev).data_ptr(), T, K, E, P, ntpp.data_ptr(),
+                                   ntpe.data_ptr(), itip.data_ptr(), ninv.data_ptr(), ws.data_ptr(),
+                                   nbytes, h, ep._stream())
+    assert rc == ep.EP_OK, ep.ep_last_error()
+    cap = T * K
+    recv = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    t_w = torch.from_numpy(w).to(dev)
+    rc = ep.ep_dispatch(_bf16_tensor(x, dev).data_ptr(), t_w.data_ptr(), H, 0, recv.data_ptr(), None,
+                        cap, h, ep._stream())
+    assert rc == ep.EP_OK, ep.ep_last_error()
+    ref = oracle.run_all(idx, w, x, E, P, False)
+    N = ref["N"]
+    y = workloads.random_rows(83, max(N, 1), H, "normal")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    assert ep.ep_combine(_bf16_tensor(y, dev).data_ptr(), h, None, out.data_ptr(), ep._stream()) == ep.EP_OK
+    torch.cuda.synchronize()
+    a = itip.cpu().numpy()
+    assert np.array_equal(a[:T * P].reshape(T, P), ref["is_token_in_partition"])
+    assert np.all(a[T * P:] == 0xC3)
+    for t, n, want in ((ntpp, P, ref["num_tokens_per_partition"]), (ntpe, E, ref["num_tokens_per_expert"]),
+                       (ninv, 1, np.array([ref["num_invalid"]]))):
+        v = t.cpu().numpy()
+        assert np.array_equal(v[:n], want) and np.all(v[n:] == -123)
+    wsb = ws.cpu().numpy()
+    base = ws.data_ptr()
+    off = lambda p: p - base
+    regions = sorted([(off(h.pair_code), T * K * 4), (off(h.slot), T * K * 4),
+                      (off(h.src_token), N * 4), (off(h.weights), T * K * 4)])
+    ends = [r[0] for r in regions[1:]] + [nbytes]
+    for (start, used), end in zip(regions, ends):
+        gap = wsb[start + used:end]
+        if end > off(h.expert_offset) > start:           # offsets + status sit between two arrays
+            gap = wsb[start + used:off(h.expert_offset)]
+        assert np.all(gap == 0xE7), (start, used, end)
+    assert np.array_equal(_bits(out), oracle.combine(y[:N], ref["slot"], w))
