@@ -32,6 +32,8 @@ EP_EHIP = -2
 EP_ECAPACITY = -3
 EP_EIDS = -4
 EP_HANDLE_MAGIC = 0x31485045
+EP_MAX_LL_TOKENS = 256
+EP_NOALLOC_SCRATCH_BYTES = 81920
 
 
 class EpError(RuntimeError):
@@ -94,6 +96,8 @@ _SIGS = {
     "ep_dispatch_backward_fp8": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P], _I),
     "ep_low_latency_dispatch": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                                  _P, ctypes.c_size_t, ctypes.POINTER(ep_handle_t), _P], _I),
+    "ep_low_latency_dispatch_noalloc": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
+                                         _P, ctypes.POINTER(ep_handle_t), _P], _I),
     "ep_combine": ([_P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_dispatch_backward": ([_P, ctypes.POINTER(ep_handle_t), _P, _P], _I),
     "ep_combine_backward": ([_P, _P, ctypes.POINTER(ep_handle_t), _P, _P, _P, _P], _I),
@@ -167,6 +171,18 @@ def ep_low_latency_dispatch(x, topk_idx, topk_weights, num_tokens, hidden, num_t
                                           num_tokens_per_partition, num_tokens_per_expert,
                                           is_token_in_partition, num_invalid, ws, ws_bytes,
                                           ctypes.byref(handle), stream)
+
+
+def ep_low_latency_dispatch_noalloc(x, topk_idx, topk_weights, num_tokens, hidden, num_topk,
+                                    num_experts, num_partitions, use_fp8, num_max_tokens, recv_x,
+                                    recv_scales, num_tokens_per_partition, num_tokens_per_expert,
+                                    is_token_in_partition, num_invalid, handle, stream) -> int:
+    return load().ep_low_latency_dispatch_noalloc(x, topk_idx, topk_weights, num_tokens, hidden,
+                                                  num_topk, num_experts, num_partitions,
+                                                  int(use_fp8), num_max_tokens, recv_x, recv_scales,
+                                                  num_tokens_per_partition, num_tokens_per_expert,
+                                                  is_token_in_partition, num_invalid,
+                                                  ctypes.byref(handle), stream)
 
 
 def ep_get_dispatch_layout_aligned(topk_idx, num_tokens, num_topk, num_experts, num_partitions,

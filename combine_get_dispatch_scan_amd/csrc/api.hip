@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -332,14 +333,13 @@ int ep_dispatch_ex(const void* x, const float* x_scales, const float* topk_weigh
     return EP_OK;
 }
 
-int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
-                            int T, int H, int K, int E, int P, int use_fp8, int cap,
-                            void* recv_x, float* recv_scales,
-                            int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
-                            uint8_t* is_token_in_partition, int32_t* num_invalid,
-                            void* ws, size_t ws_bytes, ep_handle_t* handle, hipStream_t stream)
+// Arguments of the low-latency dispatch other than the workspace; no HIP call.
+static int ll_check(const void* x, const int64_t* topk_idx, const float* topk_weights, int T, int H,
+                    int K, int E, int P, int use_fp8, int cap, const void* recv_x,
+                    const float* recv_scales, const int32_t* num_tokens_per_partition,
+                    const int32_t* num_tokens_per_expert, const uint8_t* is_token_in_partition,
+                    const int32_t* num_invalid, const ep_handle_t* handle)
 {
-    g_err.clear();
     int rc = check_dims(T, K, E, P);
     if (rc)
         return rc;
@@ -360,12 +360,31 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
         return fail(EP_EINVAL, "count outputs must be non-NULL 4-byte aligned device pointers");
     if (topk_weights && !aligned(topk_weights, 4))
         return fail(EP_EINVAL, "topk_weights must be 4-byte aligned");
-    const WsLayout L = ws_layout(T, K, E, P);
-    if (!ws || !aligned(ws, kAlign))
-        return fail(EP_EINVAL, "workspace must be a non-NULL 256-byte aligned device pointer");
-    if (ws_bytes < L.total)
-        return fail(EP_EINVAL, "workspace too small: %zu bytes given, %zu needed", ws_bytes, L.total);
+    ep_handle_t probe;               // the dimensions check_rows reads
+    memset(&probe, 0, sizeof probe);
+    probe.num_tokens = T;
+    probe.num_topk = K;
+    probe.num_experts = E;
+    probe.static_cap = cap;
+    rc = check_rows(&probe, x, H, use_fp8, recv_x, recv_scales, 0);
+    if (rc)
+        return rc;
+    if (T > 0 && (!recv_x || !aligned(recv_x, 16)))
+        return fail(EP_EINVAL, "recv_x must be a non-NULL 16-byte aligned device pointer");
+    if (T > 0 && use_fp8 && (!recv_scales || !aligned(recv_scales, 4)))
+        return fail(EP_EINVAL, "recv_scales must be a non-NULL 4-byte aligned device pointer");
+    return EP_OK;
+}
 
+// The low-latency dispatch on checked arguments, with its handle arrays in
+// the workspace `ws`.
+static int ll_run(const void* x, const int64_t* topk_idx, const float* topk_weights, int T, int H,
+                  int K, int E, int P, int use_fp8, int cap, void* recv_x, float* recv_scales,
+                  int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
+                  uint8_t* is_token_in_partition, int32_t* num_invalid, void* ws, size_t ws_bytes,
+                  ep_handle_t* handle, hipStream_t stream)
+{
+    const WsLayout L = ws_layout(T, K, E, P);
     char* w = static_cast<char*>(ws);
     ep_handle_t h;
     memset(&h, 0, sizeof h);
@@ -384,13 +403,6 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
     h.static_cap = cap;
     h.weights = reinterpret_cast<float*>(w + L.weights);
     h.status = reinterpret_cast<int32_t*>(w + L.status);
-    rc = check_rows(&h, x, H, use_fp8, recv_x, recv_scales, 0);
-    if (rc)
-        return rc;
-    if (T > 0 && (!recv_x || !aligned(recv_x, 16)))
-        return fail(EP_EINVAL, "recv_x must be a non-NULL 16-byte aligned device pointer");
-    if (T > 0 && use_fp8 && (!recv_scales || !aligned(recv_scales, 4)))
-        return fail(EP_EINVAL, "recv_scales must be a non-NULL 4-byte aligned device pointer");
 
     moe_ep::LowLatencyLaunch LL;
     LL.x = x;
@@ -424,6 +436,107 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
     h.dispatch_seq = 1;         // the kernel writes 1 or 0 into the overflow word
     *handle = h;
     return EP_OK;
+}
+
+int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                            int T, int H, int K, int E, int P, int use_fp8, int cap,
+                            void* recv_x, float* recv_scales,
+                            int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_partition, int32_t* num_invalid,
+                            void* ws, size_t ws_bytes, ep_handle_t* handle, hipStream_t stream)
+{
+    g_err.clear();
+    int rc = ll_check(x, topk_idx, topk_weights, T, H, K, E, P, use_fp8, cap, recv_x, recv_scales,
+                      num_tokens_per_partition, num_tokens_per_expert, is_token_in_partition,
+                      num_invalid, handle);
+    if (rc)
+        return rc;
+    const WsLayout L = ws_layout(T, K, E, P);
+    if (!ws || !aligned(ws, kAlign))
+        return fail(EP_EINVAL, "workspace must be a non-NULL 256-byte aligned device pointer");
+    if (ws_bytes < L.total)
+        return fail(EP_EINVAL, "workspace too small: %zu bytes given, %zu needed", ws_bytes, L.total);
+    return ll_run(x, topk_idx, topk_weights, T, H, K, E, P, use_fp8, cap, recv_x, recv_scales,
+                  num_tokens_per_partition, num_tokens_per_expert, is_token_in_partition,
+                  num_invalid, ws, ws_bytes, handle, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free low-latency dispatch keeps its handle arrays in one
+// device array per GPU (`scratch`), instead of a caller workspace.  Host code
+// never passes `scratch` itself to a kernel or a copy -- on the host that name
+// is only a stand-in -- but the device address hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = EP_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's `scratch` (looked up on the first call per
+// device).  Returns EP_OK and sets *ptr, or an error code.
+int scratch_address(void** ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(EP_EINVAL, "device %d is beyond the %d devices the scratch table covers", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, kAlign))
+            return fail(EP_EHIP, "scratch array has no 256-byte aligned device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_low_latency_dispatch_noalloc(const void* x, const int64_t* topk_idx,
+                                    const float* topk_weights, int T, int H, int K, int E, int P,
+                                    int use_fp8, int cap, void* recv_x, float* recv_scales,
+                                    int32_t* num_tokens_per_partition,
+                                    int32_t* num_tokens_per_expert,
+                                    uint8_t* is_token_in_partition, int32_t* num_invalid,
+                                    ep_handle_t* handle, hipStream_t stream)
+{
+    g_err.clear();
+    int rc = ll_check(x, topk_idx, topk_weights, T, H, K, E, P, use_fp8, cap, recv_x, recv_scales,
+                      num_tokens_per_partition, num_tokens_per_expert, is_token_in_partition,
+                      num_invalid, handle);
+    if (rc)
+        return rc;
+    const size_t need = ws_layout(T, K, E, P).total;
+    if (need > kScratchBytes)
+        return fail(EP_EINVAL, "T=%d K=%d E=%d P=%d need %zu bytes of scratch; the allocation-free "
+                    "dispatch holds %zu (use ep_low_latency_dispatch with a workspace)",
+                    T, K, E, P, need, kScratchBytes);
+    void* ptr = nullptr;
+    rc = scratch_address(&ptr);
+    if (rc)
+        return rc;
+    // every array the kernel leaves in the scratch (slots, weight copy,
+    // offsets, status) is written whole by the launch: nothing must start at 0
+    return ll_run(x, topk_idx, topk_weights, T, H, K, E, P, use_fp8, cap, recv_x, recv_scales,
+                  num_tokens_per_partition, num_tokens_per_expert, is_token_in_partition,
+                  num_invalid, ptr, kScratchBytes, handle, stream);
 }
 
 int ep_dispatch_cached(const void* x, const ep_handle_t* handle, void* recv_x, float* recv_scales,

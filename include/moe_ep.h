@@ -61,6 +61,10 @@ extern "C" {
 #define EP_MAX_HIDDEN      32768
 
 #define EP_MAX_LL_TOKENS   256     /* tokens per ep_low_latency_dispatch call     */
+#define EP_NOALLOC_SCRATCH_BYTES 81920   /* per-GPU array of the allocation-free
+                                            low-latency dispatch: the handle
+                                            arrays of T=256, K=16, E=1024, P=64
+                                            take 78592 bytes                  */
 #define EP_MAX_ALIGNMENT   1024    /* expert_alignment of an aligned layout        */
 
 #define EP_HANDLE_MAGIC    0x31485045u   /* "EPH1" */
@@ -221,6 +225,35 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
                             int32_t* num_tokens_per_partition, int32_t* num_tokens_per_expert,
                             uint8_t* is_token_in_partition, int32_t* num_invalid,
                             void* ws, size_t ws_bytes, ep_handle_t* handle, hipStream_t stream);
+
+/*
+ * Allocation-free low-latency dispatch, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The same launch and results as
+ * ep_low_latency_dispatch, but the handle's arrays (slots, weight copy,
+ * expert offsets, status) live in a library-owned device array of
+ * EP_NOALLOC_SCRATCH_BYTES on each GPU instead of a caller workspace.  The
+ * call allocates nothing; the array is set up on the first call on each
+ * device (a symbol lookup) and stays until the process ends.
+ *
+ * Arguments as for ep_low_latency_dispatch, without ws / ws_bytes; the
+ * current device must be the device of `stream`.  Every call on one GPU uses
+ * that GPU's one array, which keeps the latest call's contents: the handle
+ * stays valid (for ep_combine, ep_dispatch_cached, the backward calls,
+ * ep_handle_recv_counts) until the next call of this entry point on the same
+ * GPU, and calls that overlap on one GPU (several streams or host threads)
+ * race.  A captured graph replays into the same array.
+ * Errors: EP_EINVAL (as ep_low_latency_dispatch; dimensions whose arrays do
+ * not fit the scratch, which the stated limits never produce), EP_EHIP.
+ */
+int ep_low_latency_dispatch_noalloc(const void* x, const int64_t* topk_idx,
+                                    const float* topk_weights, int num_tokens, int hidden,
+                                    int num_topk, int num_experts, int num_partitions,
+                                    int use_fp8, int num_max_tokens, void* recv_x,
+                                    float* recv_scales, int32_t* num_tokens_per_partition,
+                                    int32_t* num_tokens_per_expert,
+                                    uint8_t* is_token_in_partition, int32_t* num_invalid,
+                                    ep_handle_t* handle, hipStream_t stream);
 
 /*
  * GEMM-facing layout options (GeekNews, "Những thay đổi chính của bản phát

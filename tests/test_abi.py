@@ -310,3 +310,22 @@ def test_fp8_combine_calls_validate_before_any_hip_call():
     h2.hidden = 136
     assert ep.ep_dispatch_backward_fp8(FAKE, FAKE, h2, FAKE, None) == ep.EP_EINVAL
     assert "hidden % 128" in ep.ep_last_error()
+
+
+def test_noalloc_scratch_covers_every_low_latency_call():
+    """The allocation-free dispatch's per-GPU array holds the handle arrays
+    of the largest low-latency call the limits allow, the header and the
+    binding agree on its size, and arguments are checked before any HIP call."""
+    hdr = open(os.path.join(ROOT, "include", "moe_ep.h")).read()
+    assert re.search(r"#define EP_NOALLOC_SCRATCH_BYTES\s+(\d+)", hdr).group(1) == str(ep.EP_NOALLOC_SCRATCH_BYTES)
+    assert re.search(r"#define EP_MAX_LL_TOKENS\s+(\d+)", hdr).group(1) == str(ep.EP_MAX_LL_TOKENS)
+    need = ep.ep_workspace_bytes(ep.EP_MAX_LL_TOKENS, 16, 1024, 64)
+    assert 0 < need <= ep.EP_NOALLOC_SCRATCH_BYTES, need
+    h = ep.ep_handle_t()
+    for args in [(300, 128, 2, 8, 2, 0, 4), (16, 128, 2, 8, 3, 0, 4), (16, 100, 2, 8, 2, 1, 4),
+                 (16, 128, 2, 8, 2, 0, 0)]:
+        T, H, K, E, P, fp8, cap = args
+        rc = ep.ep_low_latency_dispatch_noalloc(FAKE, FAKE, None, T, H, K, E, P, fp8, cap, FAKE, FAKE,
+                                                FAKE, FAKE, FAKE, FAKE, h, None)
+        assert rc == ep.EP_EINVAL, args
+        assert ep.ep_last_error()
