@@ -11,6 +11,8 @@
 // the token's receive rows and weights, which are broadcast to the wave as
 // scalars.  Each lane owns 8 channels per wave step; all K 16-byte gathers of
 // a step (and of kCombineUnroll steps) are issued before the first fma.
+#include <stdlib.h>
+
 #include "device.h"
 #include "launch.h"
 
@@ -63,6 +65,7 @@ struct CombineArgs {
     const uint16_t* y;
     int T, H, K;
     int nseg, iters_per_seg, iters;
+    int g;                    // tokens per workgroup of the token-owner form
     const int32_t* slot;
     const float* w;
     uint16_t* out;
@@ -138,6 +141,109 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
             }
         }
     }
+}
+
+// Token-owner form: a workgroup of kOwnerWaves waves owns `g` whole tokens.
+// Wave w takes the 512-channel steps w, w + W, w + 2W, ... of the workgroup's
+// g * S steps (S steps per token), two at a time.  Each step gathers its K row
+// pieces, reduces them exactly as combine_kernel does (same fma order), and
+// leaves its 1 KB of BF16 results in LDS; after a barrier the workgroup writes
+// its g output rows as one contiguous piece.
+constexpr int kOwnerWaves = 16;
+constexpr int kOwnerStreamAux = 18;              // nt | sc1: outputs past the Infinity Cache
+constexpr int kOwnerLdsBytes = 65536;            // g * H * 2 bytes of staged output at most
+
+template <int KMAX, bool UNIT>
+__device__ __forceinline__ void owner_meta(const CombineArgs& a, int t, int (&sk)[KMAX], float (&wk)[KMAX])
+{
+    const int lane = lane_id();
+    int s_own = -1;
+    float w_own = 0.0f;
+    if (lane < a.K) {
+        s_own = a.slot[(size_t)t * a.K + lane];
+        w_own = UNIT ? 1.0f : a.w[(size_t)t * a.K + lane];
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        sk[k] = k < a.K ? readlane(s_own, k) : -1;
+        wk[k] = k < a.K ? readlane_f(w_own, k) : 0.0f;
+    }
+}
+
+template <int KMAX, bool UNIT, int AUX>
+__global__ __launch_bounds__(kOwnerWaves * kWave) void combine_owner_kernel(CombineArgs a)
+{
+    extern __shared__ u32x4 lds_out[];                  // [g][H / 8]
+    const int wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int H = a.H;
+    const int S = a.iters;
+    const int t0 = blockIdx.x * a.g;
+    const int ntok = min(a.g, a.T - t0);
+    const int nsteps = ntok * S;
+    for (int s0 = wave; s0 < nsteps; s0 += 2 * kOwnerWaves) {
+        const int s1 = s0 + kOwnerWaves;
+        const bool has1 = s1 < nsteps;
+        const int g0 = s0 / S, g1 = s1 / S;
+        int sk0[KMAX], sk1[KMAX];
+        float wk0[KMAX], wk1[KMAX];
+        owner_meta<KMAX, UNIT>(a, t0 + g0, sk0, wk0);
+        owner_meta<KMAX, UNIT>(a, t0 + (has1 ? g1 : g0), sk1, wk1);
+        const int cb0 = (s0 - g0 * S) * kCombineChPerIter + lane * 8;
+        const int cb1 = (s1 - g1 * S) * kCombineChPerIter + lane * 8;
+        const bool act0 = cb0 < H;
+        const bool act1 = has1 && cb1 < H;
+        u32x4 d0[KMAX], d1[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (sk0[k] >= 0 && act0)
+                d0[k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk0[k] * H + cb0);
+            if (sk1[k] >= 0 && act1)
+                d1[k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk1[k] * H + cb1);
+        }
+        float acc0[8], acc1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            acc0[j] = 0.0f;
+            acc1[j] = 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (sk0[k] >= 0 && act0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc0[2 * j] = __builtin_fmaf(wk0[k], bf16_lo(d0[k][j]), acc0[2 * j]);
+                    acc0[2 * j + 1] = __builtin_fmaf(wk0[k], bf16_hi(d0[k][j]), acc0[2 * j + 1]);
+                }
+            }
+            if (sk1[k] >= 0 && act1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc1[2 * j] = __builtin_fmaf(wk1[k], bf16_lo(d1[k][j]), acc1[2 * j]);
+                    acc1[2 * j + 1] = __builtin_fmaf(wk1[k], bf16_hi(d1[k][j]), acc1[2 * j + 1]);
+                }
+            }
+        }
+        if (act0) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = pack_bf16x2(acc0[2 * j], acc0[2 * j + 1]);
+            lds_out[(g0 * H + cb0) / 8] = o;
+        }
+        if (act1) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = pack_bf16x2(acc1[2 * j], acc1[2 * j + 1]);
+            lds_out[(g1 * H + cb1) / 8] = o;
+        }
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t orow = make_rsrc(a.out + (size_t)t0 * H, ntok * H * 2);
+    const int n16 = ntok * H / 8;
+    for (int i = threadIdx.x; i < n16; i += kOwnerWaves * kWave)
+        buffer_store16<AUX>(lds_out[i], orow, i * 16);
 }
 
 // Combine of FP8 rows: every gathered element is first widened to
@@ -346,6 +452,20 @@ hipError_t launch_combine_fp8(const void* y, const float* scales, int scale_ld, 
     return hipGetLastError();
 }
 
+// Which form of the BF16 combine runs: the token-owner form for outputs
+// past EP_COMBINE_STREAM_OUT_BYTES, the segmented form otherwise.
+// EP_COMBINE_OWNER=1 / 0 in the environment forces one form (read at every
+// launch; for tests and measurements).
+static bool use_owner_form(bool stream_out)
+{
+    const char* v = getenv("EP_COMBINE_OWNER");
+    if (v && v[0] == '1')
+        return true;
+    if (v && v[0] == '0')
+        return false;
+    return stream_out;
+}
+
 hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slot,
                           const float* w, void* out, hipStream_t stream)
 {
@@ -367,6 +487,31 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const int32_t* slo
     dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
     dim3 block(kCombineWaves * kWave);
     const bool stream_out = (long long)T * H * 2 > EP_COMBINE_STREAM_OUT_BYTES;
+    if (use_owner_form(stream_out)) {
+        a.g = min(4, kOwnerLdsBytes / (H * 2));        // >= 1: H <= 32768
+        dim3 og((unsigned)((T + a.g - 1) / a.g));
+        dim3 ob(kOwnerWaves * kWave);
+        const size_t lds = (size_t)a.g * H * 2;
+#define EP_OWNER_A(KM, AUX)                                                                                \
+    do {                                                                                                   \
+        if (w) hipLaunchKernelGGL((combine_owner_kernel<KM, false, AUX>), og, ob, lds, stream, a);         \
+        else hipLaunchKernelGGL((combine_owner_kernel<KM, true, AUX>), og, ob, lds, stream, a);            \
+    } while (0)
+#define EP_OWNER(KM)                                                                                       \
+    do {                                                                                                   \
+        debug_launch(stream_out ? "combine_owner_kernel<nt>" : "combine_owner_kernel", og, ob, lds);       \
+        if (stream_out) EP_OWNER_A(KM, kOwnerStreamAux);                                                   \
+        else EP_OWNER_A(KM, EP_COMBINE_STORE_AUX);                                                         \
+    } while (0)
+        if (K <= 2) EP_OWNER(2);
+        else if (K <= 4) EP_OWNER(4);
+        else if (K <= 8) EP_OWNER(8);
+        else EP_OWNER(16);
+#undef EP_OWNER
+#undef EP_OWNER_A
+        return hipGetLastError();
+    }
+    a.g = 0;
 #define EP_COMBINE_A(KM, AUX)                                                                   \
     do {                                                                                        \
         if (w) hipLaunchKernelGGL((combine_kernel<KM, false, AUX>), grid, block, 0, stream, a); \

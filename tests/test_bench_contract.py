@@ -85,3 +85,33 @@ def test_parity_verdict_on_the_oracle_itself_and_planted_mistakes(name):
     if wl.use_fp8:
         g["scales"][0, 0] = np.nextafter(g["scales"][0, 0], np.float32(np.inf))
         assert bench.parity_verdict(g, ref, N, True)["recv_scales"] == "MISMATCH"
+
+
+@pytest.mark.parametrize("wl", [workloads.config("tiny"),
+                                workloads.Workload("bench_mt_fp8", 300, 512, 32, 4, 8, True, 91, "softmax")],
+                         ids=["tiny-bf16", "fp8"])
+def test_threaded_oracle_leg_matches_the_single_thread_run(wl):
+    """The threaded CPU-baseline leg runs the oracle's own functions on token
+    shards: its bytes must equal the single-threaded run's, and a planted
+    difference in the reference must be reported."""
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    y = workloads.expert_outputs(wl, N)
+    _, n, ref = bench.cpu_baseline(wl, idx, w, x, y, 1)
+    assert n == N
+    for threads in (1, 3, 7):
+        sec, same = bench.cpu_baseline_threaded(wl, idx, w, x, y, 1, threads, ref)
+        assert same and sec > 0, threads
+    ref["out"][wl.T // 2, 3] ^= 1
+    assert not bench.cpu_baseline_threaded(wl, idx, w, x, y, 1, 3, ref)[1]
+
+
+def test_cold_record_fields():
+    wl = workloads.config("v3")
+    bc = bench.byte_counts(wl, wl.T * wl.K)
+    rec = bench.cold_record(bc, bc["dispatch_logical"] + bc["combine_logical"], [300.0] * 10,
+                            [100.0] * 10, [180.0] * 10, "dispatch_fp8_kernel")
+    assert rec["step_us"]["median"] == 300.0
+    assert rec["roofline"]["combine"]["frac"] == round(bc["combine_alg"] / 180e-6 / 1e9 / 8000, 4)
+    assert rec["roofline"]["dispatch"]["kernel"] == "dispatch_fp8_kernel"
+    assert rec["value"] == round((bc["dispatch_logical"] + bc["combine_logical"]) / 300e-6 / 1e9, 2)

@@ -25,6 +25,8 @@ KERNELS = {
     "combine_fp8_kernel<8, weighted>": "_ZN6moe_ep18combine_fp8_kernelILi8ELb0ELb0EEEvNS_14CombineFp8ArgsE",
     "combine_fp8_kernel<8, unit, row buffers>": "_ZN6moe_ep18combine_fp8_kernelILi8ELb1ELb1EEEvNS_14CombineFp8ArgsE",
     "combine_fp8_kernel<4, unit, row buffers>": "_ZN6moe_ep18combine_fp8_kernelILi4ELb1ELb1EEEvNS_14CombineFp8ArgsE",
+    "combine_owner_kernel<8, weighted, nt|sc1 stores>": "_ZN6moe_ep20combine_owner_kernelILi8ELb0ELi18EEEvNS_11CombineArgsE",
+    "combine_owner_kernel<8, unit, nt|sc1 stores>": "_ZN6moe_ep20combine_owner_kernelILi8ELb1ELi18EEEvNS_11CombineArgsE",
 }
 
 ROW_LOAD = re.compile(r"^(global_load_dwordx4|buffer_load_dwordx4)\b")

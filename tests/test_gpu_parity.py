@@ -571,3 +571,23 @@ def test_no_writes_past_any_output(ep):
             gap = wsb[start + used:off(h.expert_offset)]
         assert np.all(gap == 0xE7), (start, used, end)
     assert np.array_equal(_bits(out), oracle.combine(y[:N], ref["slot"], w))
+
+
+@pytest.mark.parametrize("T,H,K,E,P", [(1, 256, 4, 8, 2), (333, 1000, 16, 64, 8), (257, 7168, 8, 256, 8),
+                                       (5, 32768, 2, 4, 1), (130, 4104, 6, 32, 4)])
+def test_token_owner_form_of_combine(ep, monkeypatch, T, H, K, E, P):
+    """The token-owner combine (whole tokens per workgroup, output staged in
+    LDS; the default past 160 MB of output) forced on small shapes: ragged
+    token tails, hidden sizes off the 512-channel step, one token of 32768
+    channels per workgroup, K = 16, masked and invalid ids.  Combine and the
+    backward of dispatch against the oracle, bit for bit."""
+    monkeypatch.setenv("EP_COMBINE_OWNER", "1")
+    dev = _dev()
+    idx, w = workloads.random_case(T + H, T, E, K, mask_frac=0.1, invalid_frac=0.03, dup_frac=0.03,
+                                   distinct=False)
+    x = workloads.random_rows(T + 7, T, H, "wide" if H % 128 == 0 else "bits")
+    ref, got = check(ep, idx, w, x, E, P, False, tag="owner-form")
+    g = workloads.random_rows(T + 8, T * K, H, "normal")
+    gx = ep.dispatch_backward(_bf16_tensor(g, dev), got["handle"])
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(gx), oracle.dispatch_backward(g[:ref["rows"]], ref["slot"]))
