@@ -480,14 +480,25 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];
 
-// Device address of this device's `scratch` (looked up on the first call per
-// device).  Returns EP_OK and sets *ptr, or an error code.
-int scratch_address(void** ptr)
+// Device address of the current device's `scratch` (looked up on the first
+// call per device).  A stream of another device is refused: the array the
+// kernel would reach is the current device's.  Returns EP_OK and sets *ptr,
+// or an error code.
+int scratch_address(hipStream_t stream, void** ptr)
 {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return hip_fail(e, "hipGetDevice");
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamGetDevice");
+        if (sdev != dev)
+            return fail(EP_EINVAL, "the stream belongs to device %d but device %d is current: make the "
+                        "stream's device current first", (int)sdev, dev);
+    }
     if (dev < 0 || dev >= kMaxDevices)
         return fail(EP_EINVAL, "device %d is beyond the %d devices the scratch table covers", dev,
                     kMaxDevices);
@@ -529,7 +540,7 @@ int ep_low_latency_dispatch_noalloc(const void* x, const int64_t* topk_idx,
                     "dispatch holds %zu (use ep_low_latency_dispatch with a workspace)",
                     T, K, E, P, need, kScratchBytes);
     void* ptr = nullptr;
-    rc = scratch_address(&ptr);
+    rc = scratch_address(stream, &ptr);
     if (rc)
         return rc;
     // every array the kernel leaves in the scratch (slots, weight copy,

@@ -237,7 +237,7 @@ int ep_low_latency_dispatch(const void* x, const int64_t* topk_idx, const float*
  * device (a symbol lookup) and stays until the process ends.
  *
  * Arguments as for ep_low_latency_dispatch, without ws / ws_bytes; the
- * current device must be the device of `stream`.  Every call on one GPU uses
+ * current device must be the device of `stream` (else EP_EINVAL).  Every call on one GPU uses
  * that GPU's one array, which keeps the latest call's contents: the handle
  * stays valid (for ep_combine, ep_dispatch_cached, the backward calls,
  * ep_handle_recv_counts) until the next call of this entry point on the same
