@@ -116,7 +116,7 @@ typedef struct ep_handle {
 
 /* Library version, major*10000 + minor*100 + patch.  EP_VERSION is the
  * version of this header; ep_version() that of the loaded library. */
-#define EP_VERSION 10100
+#define EP_VERSION 10200
 int ep_version(void);
 
 /* Message describing the last error returned on this thread ("" if none). */
