@@ -1,6 +1,7 @@
 """The C ABI from plain C: tests/c_abi_driver (built with the library) runs
-layout -> dispatch (FP8 and BF16) -> counts -> combine through the HIP
-runtime only and compares every output with the CPU oracle byte for byte."""
+layout -> dispatch (FP8 and BF16) -> counts -> combine, and the
+allocation-free low-latency dispatch twice in a row, through the HIP runtime
+only, and compares every output with the CPU oracle byte for byte."""
 import os
 import subprocess
 
