@@ -76,6 +76,10 @@ def lib():
         L.oracle_dispatch_backward.restype = None
         L.oracle_combine_backward.argtypes = [P, P, i32, i32, i32, P, P, P, P]
         L.oracle_combine_backward.restype = None
+        L.oracle_rank_routing.argtypes = [P, i32, i32, i32, i32, P]
+        L.oracle_rank_routing.restype = None
+        L.oracle_pack_metadata.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P]
+        L.oracle_pack_metadata.restype = None
         _lib = L
     return _lib
 
@@ -270,6 +274,33 @@ def combine_backward(grad_out_bits: np.ndarray, y_bits, slot: np.ndarray, w: np.
     return grad_y, grad_w
 
 
+def rank_routing(topk_idx: np.ndarray, E: int, P: int) -> np.ndarray:
+    """Destination ranks of each token: int64 [T, min(K, P)], the distinct
+    partitions of its dispatched experts, ascending, then -1."""
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    Kp = min(K, P)
+    out = np.empty((T, Kp), np.int64)
+    lib().oracle_rank_routing(_p(idx), T, K, E, P, _p(out))
+    return out
+
+
+def pack_metadata(topk_idx: np.ndarray, topk_weights: np.ndarray, part_idx: np.ndarray,
+                  slot_pack: np.ndarray, rows: int, E: int, P: int, fill_idx: int = -7,
+                  fill_w: float = -7.0):
+    """Metadata of the packed rows: (local_idx int64 [rows, K], local_w fp32
+    [rows, K]); rows no pair maps to keep the fill values."""
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_weights, np.float32)
+    part = _c(part_idx, np.int64)
+    sp = _c(slot_pack, np.int32)
+    T, K = idx.shape
+    local_idx = np.full((rows, K), fill_idx, np.int64)
+    local_w = np.full((rows, K), fill_w, np.float32)
+    lib().oracle_pack_metadata(_p(idx), _p(w), _p(part), _p(sp), T, K, E, P, _p(local_idx), _p(local_w))
+    return local_idx, local_w
+
+
 def run_all(topk_idx, topk_weights, x_bits, E, P, use_fp8, capacity=None, y_bits=None, align=1):
     """The whole path on the CPU: layout, offsets, slots, dispatch and, when
     y_bits is given, combine.  Returns a dict of every intermediate.  With
@@ -288,4 +319,53 @@ def run_all(topk_idx, topk_weights, x_bits, E, P, use_fp8, capacity=None, y_bits
         res.update(recv_x=recv, recv_scales=scales)
     if y_bits is not None:
         res["out"] = combine(y_bits, slot, topk_weights)
+    return res
+
+
+def ep_one_source(topk_idx, topk_weights, x_bits, E, P, use_fp8, y_parts=None):
+    """The expert-parallel flow over P ranks for one source rank's tokens,
+    composed from the functions above (every exchange between ranks is the
+    identity here: destination p receives the packed block p).
+
+    Sender: rank_routing, then the packed rows are the dispatch of the
+    rows along part_idx (E' = P experts, one per destination, so each token
+    lands once per destination, ascending token), with their metadata.
+    Receiver p: layout and dispatch of its block along the local ids (E/P
+    local experts, one partition), the received rows taken as they are.
+    With y_parts (list of bf16 rows per destination, in p's receive order):
+    partial rows = combine with the received weights, and the origin's
+    result = the unit-weight sum of the returned rows in rank order.
+    Returns a dict of every intermediate."""
+    T, K = topk_idx.shape
+    epp = E // P
+    part = rank_routing(topk_idx, E, P)
+    Kp = part.shape[1]
+    pk = run_all(part, np.ones((T, Kp), np.float32), x_bits, P, P, use_fp8)
+    slot_pack = pk["slot"]
+    rows = pk["rows"]
+    local_idx, local_w = pack_metadata(topk_idx, topk_weights, part, slot_pack, rows, E, P)
+    off = pk["expert_offset"]
+    res = dict(part_idx=part, pack=pk, local_idx=local_idx, local_w=local_w, dest=[])
+    partials = np.zeros((rows, x_bits.shape[1] if x_bits is not None else 0), np.uint16)
+    for p in range(P):
+        r0, r1 = int(off[p]), int(off[p + 1])
+        li = np.ascontiguousarray(local_idx[r0:r1])
+        lw = np.ascontiguousarray(local_w[r0:r1])
+        d = dict(rows=(r0, r1))
+        if x_bits is not None:
+            if use_fp8:
+                ru = run_all(li, lw, None, epp, 1, True)
+                recv, scales = dispatch_fp8_input(pk["recv_x"][r0:r1], pk["recv_scales"][r0:r1], ru["slot"],
+                                                  ru["rows"])
+                ru.update(recv_x=recv, recv_scales=scales)
+            else:
+                ru = run_all(li, lw, pk["recv_x"][r0:r1], epp, 1, False)
+            d["unpack"] = ru
+            if y_parts is not None:
+                d["partial"] = combine(y_parts[p], ru["slot"], lw)
+                partials[r0:r1] = d["partial"]
+        res["dest"].append(d)
+    if y_parts is not None:
+        res["partials"] = partials
+        res["out"] = dispatch_backward(partials, slot_pack)
     return res

@@ -415,3 +415,94 @@ void oracle_combine_backward(const uint16_t* grad_out, const uint16_t* y, int T,
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Expert parallelism over P ranks, one rank's share.  With partitions as real
+ * ranks, a token goes to each rank that hosts one of its dispatched experts,
+ * once (devtrends.ru, "Как это выглядит в коде": is_token_in_rank and
+ * num_tokens_per_rank; stakiran summary section 3: dispatch, expert GEMM,
+ * combine).  Readings: the sender packs its rows partition-major, ascending
+ * token within each destination; each packed row carries the token's K
+ * expert ids as local ids of the destination (e - p*E/P, or -1 for experts
+ * elsewhere, masked or invalid) and its K weights (0 where the id is -1); the
+ * origin sums the returned per-rank rows in rank order.
+ * ------------------------------------------------------------------------ */
+
+/* part_idx [T][Kp], Kp = min(K, P): the distinct partitions of the token's
+ * dispatched experts (the validity rules of oracle_layout), ascending, then
+ * -1. */
+void oracle_rank_routing(const int64_t* topk_idx, int T, int K, int E, int P, int64_t* part_idx)
+{
+    const int epp = E / P;
+    const int Kp = K < P ? K : P;
+    uint8_t* hit = (uint8_t*)malloc((size_t)P);
+    uint8_t* seen = (uint8_t*)calloc((size_t)E, 1);
+    for (int t = 0; t < T; ++t) {
+        for (int p = 0; p < P; ++p)
+            hit[p] = 0;
+        for (int k = 0; k < K; ++k) {
+            int64_t e = topk_idx[(size_t)t * K + k];
+            if (e < 0 || e >= E || seen[e])
+                continue;
+            seen[e] = 1;
+            hit[e / epp] = 1;
+        }
+        for (int k = 0; k < K; ++k) {
+            int64_t e = topk_idx[(size_t)t * K + k];
+            if (e >= 0 && e < E)
+                seen[e] = 0;
+        }
+        int j = 0;
+        for (int p = 0; p < P; ++p)
+            if (hit[p])
+                part_idx[(size_t)t * Kp + j++] = p;
+        for (; j < Kp; ++j)
+            part_idx[(size_t)t * Kp + j] = -1;
+    }
+    free(seen);
+    free(hit);
+}
+
+/* Metadata of the packed rows: row r = slot_pack[t][j] carries token t to
+ * partition p = part_idx[t][j].  local_idx[r][k] = e - p*E/P when the token's
+ * k-th id e is dispatched (oracle_layout's rules) and lies in p, else -1;
+ * local_w[r][k] = topk_weights[t][k] there, else 0.  Rows no pair maps to are
+ * not written. */
+void oracle_pack_metadata(const int64_t* topk_idx, const float* topk_weights, const int64_t* part_idx,
+                          const int32_t* slot_pack, int T, int K, int E, int P,
+                          int64_t* local_idx, float* local_w)
+{
+    const int epp = E / P;
+    const int Kp = K < P ? K : P;
+    uint8_t* seen = (uint8_t*)calloc((size_t)E, 1);
+    uint8_t* ok = (uint8_t*)malloc((size_t)K);
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int64_t e = topk_idx[(size_t)t * K + k];
+            ok[k] = 0;
+            if (e >= 0 && e < E && !seen[e]) {
+                seen[e] = 1;
+                ok[k] = 1;
+            }
+        }
+        for (int k = 0; k < K; ++k) {
+            int64_t e = topk_idx[(size_t)t * K + k];
+            if (e >= 0 && e < E)
+                seen[e] = 0;
+        }
+        for (int j = 0; j < Kp; ++j) {
+            int64_t p = part_idx[(size_t)t * Kp + j];
+            int32_t r = slot_pack[(size_t)t * Kp + j];
+            if (p < 0 || r < 0)
+                continue;
+            for (int k = 0; k < K; ++k) {
+                int64_t e = topk_idx[(size_t)t * K + k];
+                int local = ok[k] && e / epp == p;
+                local_idx[(size_t)r * K + k] = local ? e - p * epp : -1;
+                local_w[(size_t)r * K + k] = local ? topk_weights[(size_t)t * K + k] : 0.0f;
+            }
+        }
+    }
+    free(ok);
+    free(seen);
+}

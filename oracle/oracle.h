@@ -115,6 +115,18 @@ void oracle_combine_backward(const uint16_t* grad_out, const uint16_t* y, int T,
                              const int32_t* slot, const float* w, uint16_t* grad_y,
                              float* grad_w);
 
+/* Expert parallelism over P ranks, one rank's share (partitions as ranks).
+ * Destination ranks of each token: part_idx [T][min(K,P)], the distinct
+ * partitions of its dispatched experts, ascending, then -1. */
+void oracle_rank_routing(const int64_t* topk_idx, int T, int K, int E, int P, int64_t* part_idx);
+
+/* Metadata of the packed rows: for row r = slot_pack[t][j] (destination
+ * p = part_idx[t][j]), local_idx[r][k] = e - p*E/P for the token's dispatched
+ * experts in p, else -1; local_w[r][k] = topk_weights[t][k] there, else 0. */
+void oracle_pack_metadata(const int64_t* topk_idx, const float* topk_weights, const int64_t* part_idx,
+                          const int32_t* slot_pack, int T, int K, int E, int P,
+                          int64_t* local_idx, float* local_w);
+
 #ifdef __cplusplus
 }
 #endif

@@ -109,6 +109,33 @@ static void run_case(int T, int H, int K, int E, int P, int cap_mode, int A)
     int scap = 1 + (int)(rnd() % 4);
     oracle_slots_static(idx, valid, T, K, E, scap, slot, &sovf);
 
+    /* expert parallelism over P ranks: destination routing, the pack's slots
+     * (layout and slots on the destinations) and the packed rows' metadata */
+    const int Kp = K < P ? K : P;
+    int64_t* part = xmalloc(sizeof(int64_t) * ((size_t)T * Kp > 0 ? (size_t)T * Kp : 1));
+    oracle_rank_routing(idx, T, K, E, P, part);
+    int32_t* pcnt = xmalloc(sizeof(int32_t) * P);
+    int32_t* ppc = xmalloc(sizeof(int32_t) * P);
+    uint8_t* pmask = xmalloc((size_t)T * P + 1);
+    uint8_t* pvalid = xmalloc((size_t)T * Kp + 1);
+    int32_t pinv = 0;
+    if (oracle_layout(part, T, Kp, P, P, pcnt, ppc, pmask, &pinv, pvalid) != 0 || pinv != 0) {
+        fprintf(stderr, "rank routing gave an invalid destination list\n");
+        exit(5);
+    }
+    int32_t* poff = xmalloc(sizeof(int32_t) * (P + 1));
+    oracle_expert_offsets(pcnt, P, poff);
+    const int prows = poff[P];
+    int32_t* pslot = xmalloc(sizeof(int32_t) * ((size_t)T * Kp + 1));
+    int32_t* psrc = xmalloc(sizeof(int32_t) * (prows > 0 ? prows : 1));
+    int32_t povf = 0;
+    oracle_slots(part, pvalid, T, Kp, poff, P, prows, pslot, psrc, &povf);
+    int64_t* lidx = xmalloc(sizeof(int64_t) * ((size_t)prows * K + 1));
+    float* lw = xmalloc(sizeof(float) * ((size_t)prows * K + 1));
+    oracle_pack_metadata(idx, w, part, pslot, T, K, E, P, lidx, lw);
+    free(part); free(pcnt); free(ppc); free(pmask); free(pvalid); free(poff); free(pslot); free(psrc);
+    free(lidx); free(lw);
+
     free(idx); free(w); free(x); free(cnt); free(pc); free(mask); free(valid); free(off);
     free(slot); free(src); free(q); free(sc); free(rb); free(out); free(gw);
 }

@@ -111,6 +111,22 @@ MUTANTS = [
      "double dot = 0.0;", "float dot = 0.0f;",
      [pins.test_combine_backward_grad_w_is_the_exact_dot_rounded_once,
       pins.test_combine_backward_grad_w_wide_range_within_double_bound]),
+    ("rank routing: destinations in descending order",
+     "        for (int p = 0; p < P; ++p)\n            if (hit[p])",
+     "        for (int p = P - 1; p >= 0; --p)\n            if (hit[p])",
+     [lambda: pins.test_rank_routing_against_brute_force(50, 16, 4, 4, "clean")]),
+    ("pack metadata: local id not offset by the partition's first expert",
+     "local_idx[(size_t)r * K + k] = local ? e - p * epp : -1;",
+     "local_idx[(size_t)r * K + k] = local ? e - p : -1;",
+     [lambda: pins.test_pack_metadata_against_brute_force(50, 16, 4, 4, "clean")]),
+    ("pack metadata: weights of experts elsewhere not zeroed",
+     "local_w[(size_t)r * K + k] = local ? topk_weights[(size_t)t * K + k] : 0.0f;",
+     "local_w[(size_t)r * K + k] = topk_weights[(size_t)t * K + k];",
+     [lambda: pins.test_pack_metadata_against_brute_force(50, 16, 4, 4, "clean")]),
+    ("pack metadata: repeated ids taken as local",
+     "int local = ok[k] && e / epp == p;",
+     "int local = e >= 0 && e < E && e / epp == p;",
+     [lambda: pins.test_pack_metadata_against_brute_force(200, 64, 6, 8, "dirty")]),
 ]
 
 

@@ -1093,3 +1093,151 @@ def test_combine_backward_grad_w_wide_range_within_double_bound():
             ulp = float(np.spacing(np.float32(abs(rn)))) if rn != 0 else 2.0 ** -149
             bound = 0.5 * ulp + (H - 1) * 2.0 ** -53 * mag
             assert abs(Fraction(float(gw[t, k])) - exact) <= Fraction(bound), (t, k)
+
+
+# ----------------------------------------------------------------------------
+# expert parallelism over ranks, one rank's share: destination routing, the
+# packed rows' metadata, and the flow composed from the pinned functions
+# ----------------------------------------------------------------------------
+
+def _brute_rank_routing(idx, E, P):
+    """Distinct partitions of each token's dispatched experts, ascending."""
+    T, K = idx.shape
+    epp = E // P
+    valid = _valid_independent(idx, E)
+    out = np.full((T, min(K, P)), -1, np.int64)
+    for t in range(T):
+        parts = sorted({int(idx[t, k]) // epp for k in range(K) if valid[t, k]})
+        out[t, :len(parts)] = parts
+    return out
+
+
+EP_SHAPES = [(50, 16, 4, 4), (200, 64, 6, 8), (64, 256, 8, 8), (33, 8, 16, 2), (40, 64, 3, 64), (7, 4, 2, 1)]
+
+
+def _ep_case(T, E, K, mode, seed):
+    kw = {} if mode == "clean" else dict(distinct=False, mask_frac=0.15, invalid_frac=0.05, dup_frac=0.1)
+    return workloads.random_case(seed, T, E, K, **kw)
+
+
+@pytest.mark.parametrize("mode", ["clean", "dirty"])
+@pytest.mark.parametrize("T,E,K,P", EP_SHAPES)
+def test_rank_routing_against_brute_force(T, E, K, P, mode):
+    """part_idx = the ascending distinct destination ranks of each token
+    (devtrends.ru "Как это выглядит в коде": is_token_in_rank), checked
+    against a set construction and against the layout's own mask."""
+    idx, _ = _ep_case(T, E, K, mode, T + E + K + P)
+    part = oracle.rank_routing(idx, E, P)
+    assert np.array_equal(part, _brute_rank_routing(idx, E, P))
+    mask = oracle.layout(idx, E, P)["is_token_in_partition"]
+    for t in range(T):
+        assert list(part[t][part[t] >= 0]) == list(np.nonzero(mask[t])[0])
+
+
+@pytest.mark.parametrize("mode", ["clean", "dirty"])
+@pytest.mark.parametrize("T,E,K,P", EP_SHAPES)
+def test_pack_metadata_against_brute_force(T, E, K, P, mode):
+    """Each packed row carries the token's K ids as local ids of its
+    destination (-1 for experts elsewhere, masked, out of range or repeated)
+    and the matching weights (0 elsewhere); across a token's rows the local
+    ids map back to exactly its dispatched experts."""
+    idx, w = _ep_case(T, E, K, mode, 3 * T + E + K + P)
+    epp = E // P
+    part = _brute_rank_routing(idx, E, P)
+    Kp = part.shape[1]
+    pk = oracle.run_all(part, np.ones((T, Kp), np.float32), None, P, P, False)
+    li, lw = oracle.pack_metadata(idx, w, part, pk["slot"], pk["rows"], E, P)
+    valid = _valid_independent(idx, E)
+    used = np.zeros(pk["rows"], bool)
+    for t in range(T):
+        got = []
+        for j in range(Kp):
+            p, r = int(part[t, j]), int(pk["slot"][t, j])
+            if p < 0:
+                assert r < 0
+                continue
+            used[r] = True
+            for k in range(K):
+                e = int(idx[t, k])
+                local = bool(valid[t, k]) and e // epp == p
+                assert li[r, k] == (e - p * epp if local else -1), (t, j, k)
+                assert lw[r, k] == (w[t, k] if local else 0.0), (t, j, k)
+                if li[r, k] >= 0:
+                    got.append(p * epp + int(li[r, k]))
+        assert sorted(got) == sorted(int(idx[t, k]) for k in range(K) if valid[t, k])
+    assert np.all(li[~used] == -7) and np.all(lw[~used] == -7.0)
+    # destination blocks are contiguous and in rank order, tokens ascending inside
+    off = pk["expert_offset"]
+    for p in range(P):
+        toks = [t for t in range(T) if p in part[t]]
+        rows_p = [int(pk["slot"][t, list(part[t]).index(p)]) for t in toks]
+        assert rows_p == list(range(int(off[p]), int(off[p + 1])))
+
+
+@pytest.mark.parametrize("use_fp8", [False, True])
+@pytest.mark.parametrize("T,E,K,P", [(60, 16, 4, 4), (130, 64, 6, 8), (33, 32, 8, 2)])
+def test_ep_receive_side_reproduces_the_single_level_dispatch(T, E, K, P, use_fp8):
+    """One source rank: after the pack, the identity exchange and the unpack,
+    destination p holds exactly the rows (and scales) that the single-level
+    dispatch puts in the blocks of p's experts, with the same per-expert
+    counts (the pages' dispatch over ranks delivers each token's rows to the
+    experts it chose)."""
+    H = 256
+    idx, w = _ep_case(T, E, K, "dirty", 5 * T + E)
+    x = workloads.random_rows(T + 11, T, H, "wide")
+    epp = E // P
+    single = oracle.run_all(idx, w, x, E, P, use_fp8)
+    ep_r = oracle.ep_one_source(idx, w, x, E, P, use_fp8)
+    for p in range(P):
+        u = ep_r["dest"][p]["unpack"]
+        a, b = int(single["expert_offset"][p * epp]), int(single["expert_offset"][(p + 1) * epp])
+        assert np.array_equal(u["num_tokens_per_expert"], single["num_tokens_per_expert"][p * epp:(p + 1) * epp])
+        assert u["rows"] == b - a
+        assert np.array_equal(u["recv_x"][:u["rows"]], single["recv_x"][a:b])
+        if use_fp8:
+            assert np.array_equal(u["recv_scales"][:u["rows"]].view(np.uint32),
+                                  single["recv_scales"][a:b].view(np.uint32))
+
+
+def test_ep_two_level_combine_is_combine_for_one_rank():
+    """With P = 1 the expert rank pre-reduces every pair of the token and the
+    origin adds one returned row to +0: the result is the single-level
+    combine, bit for bit, on wide-range data."""
+    T, E, K, H = 90, 32, 6, 256
+    idx, w = _ep_case(T, E, K, "dirty", 17)
+    x = workloads.random_rows(18, T, H, "normal")
+    single = oracle.run_all(idx, w, x, E, 1, False)
+    y = workloads.random_rows(19, max(single["rows"], 1), H, "wide")[:single["rows"]]
+    ep_r = oracle.ep_one_source(idx, w, x, E, 1, False, y_parts=[y])
+    assert np.array_equal(ep_r["out"], oracle.combine(y, single["slot"], w))
+
+
+@pytest.mark.parametrize("T,E,K,P", [(64, 32, 6, 4), (40, 64, 8, 8)])
+def test_ep_two_level_combine_exact_on_small_integers(T, E, K, P):
+    """Expert outputs in {-3..3} and weights in {1/2, 1, 2} keep every
+    product, partial row and sum exact (|sum| <= 48 in steps of 1/2 needs at
+    most 7 significant bits, within BF16's 8): the origin's sum in rank order
+    of the per-rank partial rows equals the single-level combine, which equals
+    the exact sum (each expert's output row is the same whichever path sends
+    it)."""
+    H = 128
+    rng = np.random.default_rng(T + K)
+    idx, _ = workloads.random_case(T, T, E, K, mask_frac=0.1)
+    w = np.array([0.5, 1.0, 2.0], np.float32)[rng.integers(0, 3, (T, K))]
+    x = workloads.random_rows(T + 1, T, H, "normal")
+    epp = E // P
+    single = oracle.run_all(idx, w, x, E, P, False)
+    y = _small_int_bf16(rng, (max(single["rows"], 1), H))[:single["rows"]]
+    off = single["expert_offset"]
+    y_parts = [y[int(off[p * epp]):int(off[(p + 1) * epp])] for p in range(P)]
+    ep_r = oracle.ep_one_source(idx, w, x, E, P, False, y_parts=y_parts)
+    want = oracle.combine(y, single["slot"], w)
+    assert np.array_equal(ep_r["out"], want)
+    exact = np.zeros((T, H))
+    yf = _f32(y).astype(np.float64)
+    for t in range(T):
+        for k in range(K):
+            s = single["slot"][t, k]
+            if s >= 0:
+                exact[t] += float(w[t, k]) * yf[s]
+    assert np.array_equal(_f32(want).astype(np.float64), exact)
