@@ -105,6 +105,8 @@ _SIGS = {
     "ep_handle_recv_counts_async": ([ctypes.POINTER(ep_handle_t), _P, _P], _I),
     "ep_recv_counts_decode": ([ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
     "ep_e4m3fn_encode": ([_P, _P, ctypes.c_int64, _P], _I),
+    "ep_rank_routing": ([_P, _I, _I, _I, _I, _P, _P], _I),
+    "ep_pack_metadata": ([_P, _P, _I, _I, _P, ctypes.POINTER(ep_handle_t), _P, _P, _P], _I),
 }
 
 
@@ -527,3 +529,51 @@ def e4m3fn_encode(v):
     out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
     _check(ep_e4m3fn_encode(_ptr(v.contiguous()), _ptr(out), v.numel(), _stream()))
     return out
+
+
+# ----------------------------------------------------------------------------
+# expert parallelism over ranks, one rank's share
+# ----------------------------------------------------------------------------
+
+def ep_rank_routing(topk_idx, num_tokens, num_topk, num_experts, num_partitions, part_idx,
+                    stream) -> int:
+    return load().ep_rank_routing(topk_idx, num_tokens, num_topk, num_experts, num_partitions,
+                                  part_idx, stream)
+
+
+def ep_pack_metadata(topk_idx, topk_weights, num_topk, num_experts, part_idx, pack_handle,
+                     local_idx, local_w, stream) -> int:
+    return load().ep_pack_metadata(topk_idx, topk_weights, num_topk, num_experts, part_idx,
+                                   ctypes.byref(pack_handle), local_idx, local_w, stream)
+
+
+def rank_routing(topk_idx, num_experts: int, num_partitions: int):
+    """Each token's distinct destination ranks, ascending, then -1: int64
+    [T, min(K, P)] on the GPU."""
+    import torch
+    T, K = topk_idx.shape
+    part = torch.empty((T, min(K, num_partitions)), dtype=torch.int64, device=topk_idx.device)
+    _check(ep_rank_routing(_ptr(topk_idx.contiguous()), T, K, num_experts, num_partitions,
+                           _ptr(part), _stream()))
+    return part
+
+
+def pack_for_ranks(x, topk_idx, topk_weights, num_experts: int, num_partitions: int,
+                   use_fp8: bool = True):
+    """The sender's side: rows packed destination-major (ascending token within
+    each destination, one row per (token, destination)) with their metadata.
+    Returns (send_x, send_scales or None, local_idx int64 [capacity, K],
+    local_w fp32 [capacity, K], pack Layout, part_idx); the pack layout's
+    num_tokens_per_expert[p] is the row count for destination p."""
+    import torch
+    part = rank_routing(topk_idx, num_experts, num_partitions)
+    lay = get_dispatch_layout(part, num_partitions, num_partitions)
+    send_x, send_scales, h = dispatch(x, None, lay, use_fp8)
+    K = topk_idx.shape[1]
+    cap = h.c.capacity_rows
+    local_idx = torch.full((cap, K), -1, dtype=torch.int64, device=x.device)
+    local_w = torch.zeros((cap, K), dtype=torch.float32, device=x.device)
+    _check(ep_pack_metadata(_ptr(topk_idx.contiguous()), _ptr(topk_weights.contiguous()), K,
+                            num_experts, _ptr(part), h.c, _ptr(local_idx), _ptr(local_w),
+                            _stream()))
+    return send_x, send_scales, local_idx, local_w, lay, part

@@ -761,6 +761,56 @@ int ep_handle_recv_counts(const ep_handle_t* handle, int32_t* host_counts, int32
     return ep_recv_counts_decode(handle, buf, host_counts, host_num_recv);
 }
 
+int ep_rank_routing(const int64_t* topk_idx, int T, int K, int E, int P, int64_t* part_idx,
+                    hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_dims(T, K, E, P);
+    if (rc)
+        return rc;
+    if (T > 0 && (!topk_idx || !aligned(topk_idx, 8)))
+        return fail(EP_EINVAL, "topk_idx must be a non-NULL 8-byte aligned device pointer");
+    if (T > 0 && (!part_idx || !aligned(part_idx, 8)))
+        return fail(EP_EINVAL, "part_idx must be a non-NULL 8-byte aligned device pointer");
+    hipError_t e = moe_ep::launch_rank_routing(topk_idx, T, K, E, P, part_idx, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "rank routing launch");
+    return EP_OK;
+}
+
+int ep_pack_metadata(const int64_t* topk_idx, const float* topk_weights, int K, int E,
+                     const int64_t* part_idx, const ep_handle_t* h, int64_t* local_idx,
+                     float* local_w, hipStream_t stream)
+{
+    g_err.clear();
+    int rc = check_handle(h, 2);
+    if (rc)
+        return rc;
+    const int T = h->num_tokens;
+    const int P = h->num_experts;          // the pack's "experts" are the destinations
+    rc = check_dims(T, K, E, P);
+    if (rc)
+        return rc;
+    const int Kp = K < P ? K : P;
+    if (h->num_topk != Kp || h->num_partitions != P || h->static_cap || h->expert_alignment > 1)
+        return fail(EP_EINVAL, "pack_handle must be a dense layout of part_idx over the %d destinations "
+                    "with top-%d (got E=%d P=%d K=%d)", P, Kp, h->num_experts, h->num_partitions,
+                    h->num_topk);
+    if (T > 0 && (!topk_idx || !aligned(topk_idx, 8) || !part_idx || !aligned(part_idx, 8)))
+        return fail(EP_EINVAL, "topk_idx and part_idx must be non-NULL 8-byte aligned device pointers");
+    if (T > 0 && (!topk_weights || !aligned(topk_weights, 4)))
+        return fail(EP_EINVAL, "topk_weights must be a non-NULL 4-byte aligned device pointer");
+    if (T > 0 && h->capacity_rows > 0 &&
+        (!local_idx || !aligned(local_idx, 8) || !local_w || !aligned(local_w, 4)))
+        return fail(EP_EINVAL, "local_idx (8-byte) and local_w (4-byte) must be non-NULL aligned device "
+                    "pointers of capacity_rows*K entries");
+    hipError_t e = moe_ep::launch_pack_metadata(topk_idx, topk_weights, part_idx, h->slot, T, K, E, P,
+                                                local_idx, local_w, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "pack metadata launch");
+    return EP_OK;
+}
+
 int ep_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream)
 {
     g_err.clear();

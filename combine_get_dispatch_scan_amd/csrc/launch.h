@@ -82,4 +82,11 @@ hipError_t launch_combine_backward(const void* grad_out, const void* y, int T, i
 
 hipError_t launch_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
+// expert parallelism over ranks: destination routing and packed-row metadata
+hipError_t launch_rank_routing(const int64_t* topk_idx, int T, int K, int E, int P, int64_t* part_idx,
+                               hipStream_t stream);
+hipError_t launch_pack_metadata(const int64_t* topk_idx, const float* topk_weights,
+                                const int64_t* part_idx, const int32_t* slot_pack, int T, int K,
+                                int E, int P, int64_t* local_idx, float* local_w, hipStream_t stream);
+
 }  // namespace moe_ep

@@ -381,6 +381,50 @@ int ep_combine_backward(const void* grad_out, const void* y, const ep_handle_t* 
                         hipStream_t stream);
 
 /*
+ * Expert parallelism over P ranks, one rank's share.  With partitions as real
+ * ranks a token goes once to each rank that hosts one of its dispatched
+ * experts (devtrends.ru, "Как это выглядит в коде": is_token_in_rank and
+ * num_tokens_per_rank; stakiran summary section 3: dispatch, expert GEMM,
+ * combine).  The exchange between ranks is not part of this library; the
+ * calls below and the single-rank calls give every step on either side of it:
+ *
+ *  sender   ep_rank_routing(topk_idx -> part_idx), then
+ *           ep_get_dispatch_layout(part_idx, T, Kp, P, P, ...) + ep_dispatch:
+ *           the packed rows, destination-major, ascending token within a
+ *           destination, each token quantised once; that layout's
+ *           num_tokens_per_expert[p] is the row count for destination p;
+ *           ep_pack_metadata: each packed row's local expert ids and weights
+ *  receiver ep_get_dispatch_layout(local_idx of the received rows, R, K, E/P,
+ *           1, ...) + ep_dispatch_ex with the received codes and scales as
+ *           FP8 input: the expert-contiguous layout of the local experts, in
+ *           receive order (source rank, then token)
+ *  expert   ep_combine(y, that handle, received local_w, partial): one BF16
+ *           row per received row, its local experts pre-reduced
+ *  origin   ep_dispatch_backward(returned partial rows in the packed order,
+ *           the pack's handle, out): each token's rows summed in rank order
+ *           (fp32 from +0, then BF16)
+ * Kp = min(K, P).
+ *
+ * ep_rank_routing: part_idx int64 [T*Kp], the distinct partitions of each
+ * token's in-range expert ids, ascending, then -1.  Errors: EP_EINVAL, EP_EHIP.
+ */
+int ep_rank_routing(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts,
+                    int num_partitions, int64_t* part_idx, hipStream_t stream);
+
+/*
+ * ep_pack_metadata: for the packed rows of pack_handle (a dense layout of
+ * part_idx over P "experts", dispatched), packed row r = slot[t][j] carries
+ * token t to p = part_idx[t][j]; local_idx[r*K + k] = e - p*E/P when the
+ * token's k-th id e is dispatched (in range, first occurrence in its row)
+ * and lies in p, else -1; local_w[r*K + k] = topk_weights[t*K + k] there,
+ * else 0.  local_idx int64 and local_w fp32 hold capacity_rows*K entries;
+ * rows no pair maps to are not written.  Errors: EP_EINVAL, EP_EHIP.
+ */
+int ep_pack_metadata(const int64_t* topk_idx, const float* topk_weights, int num_topk,
+                     int num_experts, const int64_t* part_idx, const ep_handle_t* pack_handle,
+                     int64_t* local_idx, float* local_w, hipStream_t stream);
+
+/*
  * Per-expert received counts to the host, for the grouped GEMM (GeekNews
  * usage section: handle.num_recv_tokens_per_expert_list).  Synchronises
  * `stream`.  host_counts: int32 [E] or NULL; host_num_recv: int32 [1] or NULL
