@@ -145,10 +145,15 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(CombineA
 
 // Token-owner form: a workgroup of kOwnerWaves waves owns `g` whole tokens.
 // Wave w takes the 512-channel steps w, w + W, w + 2W, ... of the workgroup's
-// g * S steps (S steps per token), two at a time.  Each step gathers its K row
+// g * S steps (S steps per token), one at a time.  Each step gathers its K row
 // pieces, reduces them exactly as combine_kernel does (same fma order), and
 // leaves its 1 KB of BF16 results in LDS; after a barrier the workgroup writes
-// its g output rows as one contiguous piece.
+// its g output rows as one contiguous piece.  One step at a time keeps the
+// kernel near 50 VGPRs for K <= 8, so two workgroups share a CU and one
+// writes while the other gathers.  Two steps at a time (93 VGPRs, one workgroup per CU) was
+// 3% faster on dense routing (large workload: 359 against 371 us) but 23%
+// slower on rows with few valid pairs (expert-parallel pre-reduction at the
+// V3 shape: 287 against 234 us), and the launcher cannot tell them apart.
 constexpr int kOwnerWaves = 16;
 constexpr int kOwnerStreamAux = 18;              // nt | sc1: outputs past the Infinity Cache
 constexpr int kOwnerLdsBytes = 65536;            // g * H * 2 bytes of staged output at most
@@ -181,62 +186,38 @@ __global__ __launch_bounds__(kOwnerWaves * kWave) void combine_owner_kernel(Comb
     const int t0 = blockIdx.x * a.g;
     const int ntok = min(a.g, a.T - t0);
     const int nsteps = ntok * S;
-    for (int s0 = wave; s0 < nsteps; s0 += 2 * kOwnerWaves) {
-        const int s1 = s0 + kOwnerWaves;
-        const bool has1 = s1 < nsteps;
-        const int g0 = s0 / S, g1 = s1 / S;
-        int sk0[KMAX], sk1[KMAX];
-        float wk0[KMAX], wk1[KMAX];
-        owner_meta<KMAX, UNIT>(a, t0 + g0, sk0, wk0);
-        owner_meta<KMAX, UNIT>(a, t0 + (has1 ? g1 : g0), sk1, wk1);
-        const int cb0 = (s0 - g0 * S) * kCombineChPerIter + lane * 8;
-        const int cb1 = (s1 - g1 * S) * kCombineChPerIter + lane * 8;
-        const bool act0 = cb0 < H;
-        const bool act1 = has1 && cb1 < H;
-        u32x4 d0[KMAX], d1[KMAX];
+    for (int s = wave; s < nsteps; s += kOwnerWaves) {
+        const int g = s / S;
+        int sk[KMAX];
+        float wk[KMAX];
+        owner_meta<KMAX, UNIT>(a, t0 + g, sk, wk);
+        const int cb = (s - g * S) * kCombineChPerIter + lane * 8;
+        const bool act = cb < H;
+        u32x4 d[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (sk[k] >= 0 && act)
+                d[k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk[k] * H + cb);
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[j] = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (sk0[k] >= 0 && act0)
-                d0[k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk0[k] * H + cb0);
-            if (sk1[k] >= 0 && act1)
-                d1[k] = load16_hint<EP_COMBINE_NT_LOAD>(a.y + (size_t)sk1[k] * H + cb1);
-        }
-        float acc0[8], acc1[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            acc0[j] = 0.0f;
-            acc1[j] = 0.0f;
-        }
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (sk0[k] >= 0 && act0) {
+            if (sk[k] >= 0 && act) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    acc0[2 * j] = __builtin_fmaf(wk0[k], bf16_lo(d0[k][j]), acc0[2 * j]);
-                    acc0[2 * j + 1] = __builtin_fmaf(wk0[k], bf16_hi(d0[k][j]), acc0[2 * j + 1]);
-                }
-            }
-            if (sk1[k] >= 0 && act1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc1[2 * j] = __builtin_fmaf(wk1[k], bf16_lo(d1[k][j]), acc1[2 * j]);
-                    acc1[2 * j + 1] = __builtin_fmaf(wk1[k], bf16_hi(d1[k][j]), acc1[2 * j + 1]);
+                    acc[2 * j] = __builtin_fmaf(wk[k], bf16_lo(d[k][j]), acc[2 * j]);
+                    acc[2 * j + 1] = __builtin_fmaf(wk[k], bf16_hi(d[k][j]), acc[2 * j + 1]);
                 }
             }
         }
-        if (act0) {
+        if (act) {
             u32x4 o;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                o[j] = pack_bf16x2(acc0[2 * j], acc0[2 * j + 1]);
-            lds_out[(g0 * H + cb0) / 8] = o;
-        }
-        if (act1) {
-            u32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = pack_bf16x2(acc1[2 * j], acc1[2 * j + 1]);
-            lds_out[(g1 * H + cb1) / 8] = o;
+                o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+            lds_out[(g * H + cb) / 8] = o;
         }
     }
     __syncthreads();
