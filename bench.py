@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="v3", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ep-share", action="store_true",
+                    help="skip the expert-parallel side figure (its pack dispatch shares the main "
+                         "dispatch's kernel and grid, so counter runs of the step leave it out)")
     ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--low-latency", action="store_true",
                     help="one-launch static-capacity dispatch (T <= 256) instead of layout + dispatch")
@@ -215,6 +218,82 @@ def parity_verdict(gpu, ref, N, use_fp8):
     verdict["combine"] = "bit-exact" if ulp == 0 else ("within 1 ulp" if ulp <= 1 else "MISMATCH")
     verdict["checked"] = "last timed step against the oracle on the full workload"
     return verdict
+
+
+def measure_ep_share(wl, t_idx, t_w, t_x, time_call):
+    """Expert parallelism over P ranks, one rank's share at this workload's
+    shape, each call timed alone (events, 10 launches, mean).  The sender
+    packs its tokens per destination; the P packed blocks, whose local ids are
+    valid for any one rank's E/P experts, stand in for the rows one rank
+    receives from P sources (the exchange itself is not on one GPU)."""
+    import torch
+    import combine_get_dispatch_scan_amd as ep
+    T, H, K, E, P = wl.T, wl.H, wl.K, wl.E, wl.P
+    Kp, epp, nb = min(K, P), E // P, H // 128
+    dev = t_x.device
+    sp = ep._stream()
+    p = lambda t: None if t is None else t.data_ptr()
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(ep.ep_last_error())
+    part = torch.empty((T, Kp), dtype=torch.int64, device=dev)
+    route = lambda: ok(ep.ep_rank_routing(p(t_idx), T, K, E, P, p(part), sp))
+    route()
+    lay = ep.get_dispatch_layout(part, P, P)
+    hp = lay.handle.c
+    cap = T * Kp
+    send = torch.empty((cap, H), dtype=torch.uint8, device=dev)
+    send_sc = torch.empty((cap, nb), dtype=torch.float32, device=dev)
+    li = torch.full((cap, K), -1, dtype=torch.int64, device=dev)
+    lw = torch.zeros((cap, K), dtype=torch.float32, device=dev)
+    pack_layout = lambda: ok(ep.ep_get_dispatch_layout(p(part), T, Kp, P, P, p(lay.num_tokens_per_partition),
+                                                       p(lay.num_tokens_per_expert), p(lay.is_token_in_partition),
+                                                       p(lay.num_invalid), p(lay.handle.ws),
+                                                       lay.handle.ws.numel(), hp, sp))
+    pack = lambda: ok(ep.ep_dispatch(p(t_x), None, H, 1, p(send), p(send_sc), cap, hp, sp))
+    pack()
+    meta = lambda: ok(ep.ep_pack_metadata(p(t_idx), p(t_w), K, E, p(part), hp, p(li), p(lw), sp))
+    meta()
+    _, R, _ = ep.handle_recv_counts(lay.handle)
+    # the receiver: all R packed rows as one rank's receive buffer
+    lay_r = ep.get_dispatch_layout(li[:R], epp, 1)
+    hr = lay_r.handle.c
+    capr = R * K
+    recv = torch.empty((capr, H), dtype=torch.uint8, device=dev)
+    recv_sc = torch.empty((capr, nb), dtype=torch.float32, device=dev)
+    unpack_layout = lambda: ok(ep.ep_get_dispatch_layout(p(li), R, K, epp, 1, p(lay_r.num_tokens_per_partition),
+                                                         p(lay_r.num_tokens_per_expert),
+                                                         p(lay_r.is_token_in_partition), p(lay_r.num_invalid),
+                                                         p(lay_r.handle.ws), lay_r.handle.ws.numel(), hr, sp))
+    unpack = lambda: ok(ep.ep_dispatch_ex(p(send), p(send_sc), p(lw), H, 1, 0, p(recv), p(recv_sc), capr, hr, sp))
+    unpack()
+    _, Nr, _ = ep.handle_recv_counts(lay_r.handle)
+    y = torch.randn((max(Nr, 1), H), device=dev).to(torch.bfloat16)
+    partial = torch.empty((max(R, 1), H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    reduce_ = lambda: ok(ep.ep_combine(p(y), hr, None, p(partial), sp))
+    origin = lambda: ok(ep.ep_dispatch_backward(p(partial), hp, p(out), sp))
+    B, Br = (T + 255) // 256, (R + 255) // 256
+    calls = {
+        "rank_routing": (route, T * K * 8 + T * Kp * 8),
+        "pack_layout": (pack_layout, T * Kp * 12 + T * P + B * (2 * P + 1) * 4 * 2),
+        "pack_dispatch": (pack, T * H * 2 + R * (H + 4 * nb) + T * Kp * 16 + R * 4),
+        "pack_metadata": (meta, T * Kp * 12 + T * K * 12 + R * K * 12),
+        "unpack_layout": (unpack_layout, R * K * 12 + R + Br * (2 * epp + 2) * 4 * 2),
+        "unpack_dispatch": (unpack, R * (H + 4 * nb) + Nr * (H + 4 * nb) + R * K * 16 + Nr * 4),
+        "expert_prereduce": (reduce_, Nr * H * 2 + R * H * 2 + R * K * 8),
+        "origin_sum": (origin, R * H * 2 + T * H * 2 + T * Kp * 4),
+    }
+    res = {"packed_rows": int(R), "received_pairs": int(Nr),
+           "note": "one rank's share; the P packed blocks stand in for the rows received from P sources"}
+    total = 0.0
+    for name, (fn, nbytes) in calls.items():
+        ms = time_call(fn)
+        total += ms
+        res[name] = {"us": round(ms * 1e3, 2), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    res["total_us"] = round(total * 1e3, 2)
+    return res
 
 
 def cold_record(bc, logical, step_us, disp_us, comb_us, disp_kernel):
@@ -670,6 +749,14 @@ def main():
         # the timed step's handle must hold the BF16-input dispatch again
         _ok(ep.ep_dispatch(p(t_x), p(t_w), H, 1, p(recv), p(scales), cap, h, sp))
 
+    ep_share = {}
+    if wl.use_fp8 and not args.no_ep_share:
+        ep_share = measure_ep_share(wl, t_idx, t_w, t_x, time_call)
+        # the timed step's handle must hold the plain dispatch again
+        _ok(ep.ep_get_dispatch_layout(p(t_idx), T, K, E, P, p(ntpp), p(ntpe), p(itip), p(ninv),
+                                      p(ws), ws.numel(), h, sp))
+        _ok(ep.ep_dispatch(p(t_x), p(t_w), H, 1, p(recv), p(scales), cap, h, sp))
+
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     copy_gbps = rate(lambda: dst.copy_(src), 2 << 30)
@@ -712,6 +799,7 @@ def main():
         "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},
         "backward": backward,
         "gemm_layout": gemm,
+        "ep_rank_share": ep_share,
         "logical_GBps": {
             "dispatch": round(bc["dispatch_logical"] / ((phases["layout"] + phases["dispatch"]) * 1e-3) / 1e9, 1),
             "combine": round(bc["combine_logical"] / (phases["combine"] * 1e-3) / 1e9, 1),
