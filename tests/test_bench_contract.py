@@ -115,3 +115,16 @@ def test_cold_record_fields():
     assert rec["roofline"]["combine"]["frac"] == round(bc["combine_alg"] / 180e-6 / 1e9 / 8000, 4)
     assert rec["roofline"]["dispatch"]["kernel"] == "dispatch_fp8_kernel"
     assert rec["value"] == round((bc["dispatch_logical"] + bc["combine_logical"]) / 300e-6 / 1e9, 2)
+
+
+def test_launch_events_sample_about_twenty_timed_steps():
+    """Every timed step runs the whole path; events bracket the dominant
+    kernel in every stride-th step, at least once and every step up to 20."""
+    for steps in (1, 5, 20, 39):
+        assert bench.event_stride(steps) == 1
+    assert bench.event_stride(100) == 5
+    assert bench.event_stride(1000) == 50
+    for steps in (1, 7, 20, 21, 100, 333, 1000):
+        s = bench.event_stride(steps)
+        sampled = len(range(0, steps, s))
+        assert 1 <= sampled and (sampled >= 20 or sampled == steps)
