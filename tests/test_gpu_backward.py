@@ -150,3 +150,50 @@ def test_backward_with_masks_and_capacity(ep):
         used[ref["slot"][ref["slot"] >= 0]] = True
         assert np.array_equal(_bits(gy)[used], ref_gy[used])
         _check_grad_w(gw.cpu().numpy(), ref_gw, g, y, ref["slot"], H)
+
+
+@pytest.mark.parametrize("T,H,E,K,P,fp8", [
+    (0, 256, 16, 4, 4, True),            # no tokens
+    (1, 8, 4, 1, 1, False),              # the smallest row, one expert per token
+    (5, 32768, 8, 4, 2, True),           # the largest hidden size
+    (133, 776, 1024, 16, 64, False),     # K = 16 over 1024 experts in 64 partitions, H off the 512 step
+    (257, 4224, 64, 6, 8, True),         # a ragged token tail, H off the 1024-channel FP8 step
+])
+def test_backward_at_the_boundary_limits(ep, T, H, E, K, P, fp8):
+    """Both backward calls (and the FP8 dispatch backward) at the extremes the
+    boundary accepts, with masked, out-of-range and repeated ids: grad_x and
+    grad_y bit-exact, grad_w within the fp32 bound."""
+    dev = _dev()
+    idx, w = workloads.random_case(900 + T + H, T, E, K, distinct=False, mask_frac=0.1,
+                                   invalid_frac=0.03, dup_frac=0.05)
+    x = workloads.random_rows(901 + T, T, H, "normal")
+    print(f"[bwd] limits T={T} H={H} E={E} K={K} P={P} fp8={fp8}", flush=True)
+    ref = oracle.run_all(idx, w, None, E, P, fp8)
+    rows = ref["rows"]
+    h = _forward(ep, idx, w, x, E, P, fp8)
+    cap = T * K
+    gr = workloads.random_rows(902 + T, cap, H, "normal")
+    y = workloads.random_rows(903 + T, cap, H, "normal")
+    g = workloads.random_rows(904 + T, T, H, "normal")
+    gx = ep.dispatch_backward(_bf16(gr, dev), h)
+    gy, gw = ep.combine_backward(_bf16(g, dev), h, y=_bf16(y, dev))
+    torch.cuda.synchronize()
+    assert gx.shape == (T, H) and gy.shape == (cap, H) and gw.shape == (T, K)
+    assert np.array_equal(_bits(gx), oracle.dispatch_backward(gr[:rows], ref["slot"]))
+    ref_gy, ref_gw = oracle.combine_backward(g, y[:rows], ref["slot"], w, cap)
+    assert np.array_equal(_bits(gy)[:rows], ref_gy[:rows])
+    _check_grad_w_all(gw.cpu().numpy(), ref_gw, g, y, ref["slot"], H)
+    if fp8 and T > 0:
+        # FP8 dispatch backward on E4M3FN rows (random finite codes) with
+        # random positive block scales, unit weights, against the oracle
+        rng = np.random.default_rng(905 + T)
+        q = rng.integers(0, 256, (rows, H), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] ^= 1                       # no NaN codes
+        sc = np.ldexp(rng.random((rows, H // 128)) + 0.5, rng.integers(-20, 20, (rows, H // 128)))
+        sc = sc.astype(np.float32)
+        t_q, t_s = torch.from_numpy(q).to(dev), torch.from_numpy(sc).to(dev)
+        gx8 = ep.dispatch_backward_fp8(t_q, t_s, h)
+        out8 = ep.combine_fp8(t_q, t_s, h)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(gx8), oracle.combine_fp8(q, sc, ref["slot"], None))
+        assert np.array_equal(_bits(out8), oracle.combine_fp8(q, sc, ref["slot"], w))
