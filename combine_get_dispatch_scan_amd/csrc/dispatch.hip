@@ -182,6 +182,8 @@ __global__ __launch_bounds__(kDispatchWaves * kWave) void dispatch_bf16_kernel(D
                     static_cast<uint16_t*>(a.recv));
 }
 
+constexpr size_t kDispatchFp8CapLds = 32768;     // 5 workgroups per CU
+
 hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
 {
     if (L.T == 0)
@@ -228,11 +230,18 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
     const long long recv_bytes =
         (long long)L.capacity * L.H * (L.use_fp8 ? 1 : 2) + (L.use_fp8 ? (long long)L.capacity * (L.H / kQBlock) * 4 : 0);
     const bool nt_store = EP_DISPATCH_NT_STORE && recv_bytes > EP_DISPATCH_CACHED_RECV_BYTES;
+    // The quantising FP8 kernel is capped at 5 workgroups (20 waves) per CU by
+    // 32 KB of dynamic LDS that it does not touch (160 KB per CU).  At the full
+    // 8 workgroups its scattered row writes keep more requests in flight than
+    // HBM needs; capped, it was 1-2.5% faster at 8192 and 16384 tokens of 7168
+    // channels, warm and after the caches were emptied.  The BF16 copy kernel
+    // was slower capped (42.5 -> 47 us cold at 4096 x 4096), so it runs uncapped.
+    const size_t lds = (L.use_fp8 && !L.x_scales) ? kDispatchFp8CapLds : 0;
 #define EP_DISPATCH(KERNEL, KM, FRESH)                                                  \
     do {                                                                                \
-        debug_launch(nt_store ? #KERNEL "<nt>" : #KERNEL, grid, block, 0);              \
-        if (nt_store) hipLaunchKernelGGL((KERNEL<KM, FRESH, true>), grid, block, 0, stream, a); \
-        else hipLaunchKernelGGL((KERNEL<KM, FRESH, false>), grid, block, 0, stream, a);         \
+        debug_launch(nt_store ? #KERNEL "<nt>" : #KERNEL, grid, block, lds);            \
+        if (nt_store) hipLaunchKernelGGL((KERNEL<KM, FRESH, true>), grid, block, lds, stream, a); \
+        else hipLaunchKernelGGL((KERNEL<KM, FRESH, false>), grid, block, lds, stream, a);         \
     } while (0)
 #define EP_DISPATCH_K(KERNEL, FRESH)                 \
     do {                                             \
