@@ -44,7 +44,8 @@ DESCR = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 1000 for the launch-bound tiny and decode shapes, else 100)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="v3", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -56,7 +57,16 @@ def parse():
                     help="one-launch static-capacity dispatch (T <= 256) instead of layout + dispatch")
     ap.add_argument("--ll-cap", type=int, default=0,
                     help="rows per expert for --low-latency (default: T, so nothing is dropped)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = default_steps(args.config)
+    return args
+
+
+def default_steps(config):
+    """Timed steps when --steps is not given: 1000 for the shapes whose step is
+    a few tens of microseconds (tiny, decode), 100 for the others."""
+    return 1000 if config in ("tiny", "decode") else 100
 
 
 def byte_counts(wl, N):

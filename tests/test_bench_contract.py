@@ -128,3 +128,11 @@ def test_launch_events_sample_about_twenty_timed_steps():
         s = bench.event_stride(steps)
         sampled = len(range(0, steps, s))
         assert 1 <= sampled and (sampled >= 20 or sampled == steps)
+
+
+def test_default_step_counts_follow_the_launch_bound_rule():
+    """At least 1000 timed steps where a step is tens of microseconds, 100
+    for the bandwidth-bound shapes."""
+    assert bench.default_steps("tiny") == 1000 and bench.default_steps("decode") == 1000
+    for name in ("v3", "skewed", "large"):
+        assert bench.default_steps(name) == 100
