@@ -41,6 +41,25 @@ DESCR = {
 }
 
 
+# The pages' own figures for DeepEP's dispatch and combine, reported beside
+# ours as context: network-bound multi-GPU runs on NVIDIA hardware, logical
+# GB/s counting local traffic too, so not a like-for-like comparison.
+PAGES_CONTEXT = {
+    "note": "the pages' figures for network-bound DeepEP on other hardware; context, not a target",
+    "v3_shape_logical_GBps": [
+        # GeekNews (vi.news.hada.io), "Kết quả đo hiệu năng"; aikraft.ru, the benchmark table
+        {"hardware": "SM100, EP8 over NVLink, 64 SMs", "dispatch": 726, "combine": 740},
+        {"hardware": "SM100, EP8 over NVLink, 24 SMs", "dispatch": 643, "combine": 675},
+        {"hardware": "SM100, EP 8x2 over CX7 RDMA, 12 SMs", "dispatch": 90, "combine": 91},
+        {"hardware": "SM90, EP 8x2 over CX7 RDMA, 12 SMs", "dispatch": 90, "combine": 81},
+        {"hardware": "SM90, EP 8x4 over CX7 RDMA, 6-12 SMs", "dispatch": 61, "combine": 61},
+    ],
+    # devtrends.ru, performance section; stakiran summary, section 2
+    "normal_kernels_GBps": {"H800 NVLink": "150-158", "H800 RDMA": "40-50"},
+    "decode_low_latency_us": {"hardware": "H800 + CX7 400 Gb InfiniBand, EP8", "dispatch": 77, "combine": 114},
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -830,6 +849,7 @@ def main():
             "dispatch": round(bc["dispatch_logical"] / ((phases["layout"] + phases["dispatch"]) * 1e-3) / 1e9, 1),
             "combine": round(bc["combine_logical"] / (phases["combine"] * 1e-3) / 1e9, 1),
         },
+        "pages_context": PAGES_CONTEXT,
         "hbm_frac_step": round(alg_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "hbm_frac_kernels": {
             "dispatch": round(bc["dispatch_alg"] / (phases["dispatch"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
