@@ -63,7 +63,7 @@ int check_dims(int T, int K, int E, int P)
 
 WsLayout ws_layout(int T, int K, int E, int P)
 {
-    const size_t B = (size_t)(T + kChunk - 1) / kChunk;
+    const size_t B = ((size_t)T + kChunk - 1) / kChunk;
     const size_t TK = (size_t)T * K;
     WsLayout L;
     size_t o = 0;
@@ -90,6 +90,12 @@ int check_handle(const ep_handle_t* h, int min_stage)
         return fail(EP_EINVAL, "handle was not filled by ep_get_dispatch_layout");
     if (h->stage < min_stage)
         return fail(EP_EINVAL, "handle has not been dispatched yet (call ep_dispatch first)");
+    // the layout calls fill a handle only after checking its dimensions, so
+    // out-of-range ones mean a corrupted handle, whose sizes must not be used
+    if (!dims_ok(h->num_tokens, h->num_topk, h->num_experts, h->num_partitions))
+        return fail(EP_EINVAL, "handle dimensions out of range (T=%d K=%d E=%d P=%d): not a handle "
+                    "filled by the layout call", h->num_tokens, h->num_topk, h->num_experts,
+                    h->num_partitions);
     return EP_OK;
 }
 
@@ -175,7 +181,7 @@ int ep_get_dispatch_layout_aligned(const int64_t* topk_idx, int T, int K, int E,
     h.num_topk = K;
     h.num_experts = E;
     h.num_partitions = P;
-    h.num_chunks = (T + kChunk - 1) / kChunk;
+    h.num_chunks = (int)(((int64_t)T + kChunk - 1) / kChunk);
     h.ws = ws;
     h.ws_bytes = ws_bytes;
     h.expert_offset = reinterpret_cast<int32_t*>(w + L.expert_offset);
@@ -394,7 +400,7 @@ static int ll_run(const void* x, const int64_t* topk_idx, const float* topk_weig
     h.num_topk = K;
     h.num_experts = E;
     h.num_partitions = P;
-    h.num_chunks = (T + kChunk - 1) / kChunk;
+    h.num_chunks = (int)(((int64_t)T + kChunk - 1) / kChunk);
     h.ws = ws;
     h.ws_bytes = ws_bytes;
     h.expert_offset = reinterpret_cast<int32_t*>(w + L.expert_offset);
@@ -730,9 +736,11 @@ int ep_recv_counts_decode(const ep_handle_t* handle, const int32_t* host_buf,
     const int E = handle->num_experts;
     const int32_t* off = host_buf;
     const int32_t* st = host_buf + E + 1;
+    // offsets written by the scan are non-decreasing; the difference is taken
+    // modulo 2^32 so that any buffer content decodes without overflow
     if (host_counts)
         for (int i = 0; i < E; ++i)
-            host_counts[i] = off[i + 1] - off[i];
+            host_counts[i] = (int32_t)((uint32_t)off[i + 1] - (uint32_t)off[i]);
     if (host_num_recv)
         *host_num_recv = off[E];
     // the overflow word counts only when it holds this handle's latest

@@ -195,7 +195,7 @@ hipError_t launch_dispatch(const DispatchLaunch& L, hipStream_t stream)
     a.H = L.H;
     a.K = L.K;
     a.E = L.E;
-    a.B = (L.T + kChunk - 1) / kChunk;
+    a.B = (int)(((int64_t)L.T + kChunk - 1) / kChunk);
     a.align = L.align;
     a.scale_ld = L.scale_ld;
     a.seq = L.seq;

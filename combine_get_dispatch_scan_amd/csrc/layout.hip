@@ -369,7 +369,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int T, int K, int E, int P, in
                          int32_t* num_tokens_per_expert, int32_t* num_tokens_per_partition,
                          int32_t* num_invalid, int32_t* status, hipStream_t stream)
 {
-    const int B = (T + kChunk - 1) / kChunk;
+    const int B = (int)(((int64_t)T + kChunk - 1) / kChunk);
     const size_t lds = (size_t)E * kChunkWaves * sizeof(unsigned long long);
     // 8 partition bytes per 64-bit store when rows start 8-byte aligned
     const bool wide = (P % 8 == 0) && ((reinterpret_cast<uintptr_t>(is_token_in_partition) & 7) == 0);

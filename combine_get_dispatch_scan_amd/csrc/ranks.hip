@@ -85,7 +85,7 @@ hipError_t launch_rank_routing(const int64_t* topk_idx, int T, int K, int E, int
 {
     if (T == 0)
         return hipSuccess;
-    dim3 grid((unsigned)((T + 255) / 256)), block(256);
+    dim3 grid((unsigned)(((int64_t)T + 255) / 256)), block(256);
     debug_launch("rank_routing_kernel", grid, block, 0);
     hipLaunchKernelGGL(rank_routing_kernel, grid, block, 0, stream, topk_idx, T, K, E, P, part_idx);
     return hipGetLastError();
