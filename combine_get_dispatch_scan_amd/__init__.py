@@ -260,8 +260,33 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+_KINDS = {}
+
+
+def _kinds():
+    """Element types the library accepts, by the C type it reads."""
+    if not _KINDS:
+        import torch
+        _KINDS.update(bf16=(torch.bfloat16,), fp8=(torch.float8_e4m3fn, torch.uint8),
+                      f32=(torch.float32,), i64=(torch.int64,), i32=(torch.int32,),
+                      u8=(torch.uint8,))
+    return _KINDS
+
+
+def _ptr(t, kind: Optional[str] = None, name: str = "tensor") -> Optional[int]:
+    """Device address of a tensor the library reads or writes densely.  It
+    must be a GPU tensor, contiguous (rows without gaps) and, when ``kind``
+    names one, of an element type the call takes; anything else raises
+    before the call."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous: the library reads and writes rows densely")
+    if kind is not None and t.dtype not in _kinds()[kind]:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in _kinds()[kind])}, got {t.dtype}")
+    return t.data_ptr()
 
 
 @dataclass
@@ -342,9 +367,9 @@ def get_dispatch_layout(topk_idx, num_experts: int, num_partitions: int, ws=None
     itip = torch.empty((T, num_partitions), dtype=torch.uint8, device=dev)
     ninv = torch.empty(1, dtype=torch.int32, device=dev)
     h = ep_handle_t()
-    _check(ep_get_dispatch_layout_aligned(_ptr(topk_idx.contiguous()), T, K, num_experts,
+    _check(ep_get_dispatch_layout_aligned(_ptr(topk_idx.contiguous(), "i64", "topk_idx"), T, K, num_experts,
                                           num_partitions, int(expert_alignment), _ptr(ntpp),
-                                          _ptr(ntpe), _ptr(itip), _ptr(ninv), _ptr(ws), ws.numel(),
+                                          _ptr(ntpe), _ptr(itip), _ptr(ninv), _ptr(ws, "u8", "ws"), ws.numel(),
                                           h, _stream()))
     return Layout(ntpp, ntpe, itip, ninv, Handle(h, ws))
 
@@ -376,8 +401,9 @@ def dispatch(x, topk_weights, layout: Layout, use_fp8: bool, capacity_rows: Opti
     else:
         recv = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
         scales = None
-    _check(ep_dispatch_ex(_ptr(x), _ptr(x_scales), _ptr(topk_weights), H, int(use_fp8), scale_ld,
-                          _ptr(recv), _ptr(scales), cap, h.c, _stream()))
+    _check(ep_dispatch_ex(_ptr(x, "fp8" if x_scales is not None else "bf16", "x"),
+                          _ptr(x_scales, "f32", "x_scales"), _ptr(topk_weights, "f32", "topk_weights"),
+                          H, int(use_fp8), scale_ld, _ptr(recv), _ptr(scales), cap, h.c, _stream()))
     return recv, scales, h
 
 
@@ -410,8 +436,10 @@ def low_latency_dispatch(x, topk_idx, topk_weights, num_experts: int, num_partit
     else:
         recv, scales, lay = out
     h = lay.handle
-    _check(ep_low_latency_dispatch(_ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, K, E, P,
-                                   int(use_fp8), cap, _ptr(recv), _ptr(scales),
+    _check(ep_low_latency_dispatch(_ptr(x, "bf16", "x"), _ptr(topk_idx, "i64", "topk_idx"),
+                                   _ptr(topk_weights, "f32", "topk_weights"), T, H, K, E, P,
+                                   int(use_fp8), cap, _ptr(recv, "fp8" if use_fp8 else "bf16", "recv_x"),
+                                   _ptr(scales, "f32", "recv_scales"),
                                    _ptr(lay.num_tokens_per_partition),
                                    _ptr(lay.num_tokens_per_expert),
                                    _ptr(lay.is_token_in_partition), _ptr(lay.num_invalid),
@@ -431,8 +459,10 @@ def dispatch_cached(x, handle: Handle, recv_x=None, recv_scales=None, x_scales=N
     if c.use_fp8 and recv_scales is None:
         shape = (H // 128, c.scale_ld) if c.scale_ld else (cap, H // 128)
         recv_scales = torch.empty(shape, dtype=torch.float32, device=x.device)
-    _check(ep_dispatch_cached_ex(_ptr(x), _ptr(x_scales), c, _ptr(recv_x), _ptr(recv_scales),
-                                 _stream()))
+    _check(ep_dispatch_cached_ex(_ptr(x, "fp8" if (x_scales is not None or c.fp8_input) else "bf16", "x"),
+                                 _ptr(x_scales, "f32", "x_scales"),
+                                 c, _ptr(recv_x, "fp8" if c.use_fp8 else "bf16", "recv_x"),
+                                 _ptr(recv_scales, "f32", "recv_scales"), _stream()))
     return recv_x, recv_scales
 
 
@@ -442,7 +472,8 @@ def combine(y, handle: Handle, topk_weights=None, out=None):
     c = handle.c
     if out is None:
         out = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=y.device)
-    _check(ep_combine(_ptr(y), c, _ptr(topk_weights), _ptr(out), _stream()))
+    _check(ep_combine(_ptr(y, "bf16", "y"), c, _ptr(topk_weights, "f32", "topk_weights"),
+                      _ptr(out, "bf16", "out"), _stream()))
     return out
 
 
@@ -453,7 +484,8 @@ def combine_fp8(y, y_scales, handle: Handle, topk_weights=None, out=None):
     c = handle.c
     if out is None:
         out = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=y.device)
-    _check(ep_combine_fp8(_ptr(y), _ptr(y_scales), c, _ptr(topk_weights), _ptr(out), _stream()))
+    _check(ep_combine_fp8(_ptr(y, "fp8", "y"), _ptr(y_scales, "f32", "y_scales"), c,
+                          _ptr(topk_weights, "f32", "topk_weights"), _ptr(out, "bf16", "out"), _stream()))
     return out
 
 
@@ -464,7 +496,8 @@ def dispatch_backward_fp8(grad_recv, grad_scales, handle: Handle, grad_x=None):
     c = handle.c
     if grad_x is None:
         grad_x = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=grad_recv.device)
-    _check(ep_dispatch_backward_fp8(_ptr(grad_recv), _ptr(grad_scales), c, _ptr(grad_x), _stream()))
+    _check(ep_dispatch_backward_fp8(_ptr(grad_recv, "fp8", "grad_recv"), _ptr(grad_scales, "f32", "grad_scales"),
+                                    c, _ptr(grad_x, "bf16", "grad_x"), _stream()))
     return grad_x
 
 
@@ -474,7 +507,8 @@ def dispatch_backward(grad_recv, handle: Handle, grad_x=None):
     c = handle.c
     if grad_x is None:
         grad_x = torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=grad_recv.device)
-    _check(ep_dispatch_backward(_ptr(grad_recv), c, _ptr(grad_x), _stream()))
+    _check(ep_dispatch_backward(_ptr(grad_recv, "bf16", "grad_recv"), c, _ptr(grad_x, "bf16", "grad_x"),
+                                _stream()))
     return grad_x
 
 
@@ -489,8 +523,9 @@ def combine_backward(grad_out, handle: Handle, y=None, topk_weights=None, grad_y
         grad_y = torch.empty((c.capacity_rows, c.hidden), dtype=torch.bfloat16, device=dev)
     grad_w = None if y is None else torch.empty((c.num_tokens, c.num_topk), dtype=torch.float32,
                                                 device=dev)
-    _check(ep_combine_backward(_ptr(grad_out), _ptr(y), c, _ptr(topk_weights), _ptr(grad_y),
-                               _ptr(grad_w), _stream()))
+    _check(ep_combine_backward(_ptr(grad_out, "bf16", "grad_out"), _ptr(y, "bf16", "y"), c,
+                               _ptr(topk_weights, "f32", "topk_weights"), _ptr(grad_y, "bf16", "grad_y"),
+                               _ptr(grad_w, "f32", "grad_w"), _stream()))
     return grad_y, grad_w
 
 
@@ -527,7 +562,7 @@ def e4m3fn_encode(v):
     """fp32 tensor -> uint8 codes with the device encoder."""
     import torch
     out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
-    _check(ep_e4m3fn_encode(_ptr(v.contiguous()), _ptr(out), v.numel(), _stream()))
+    _check(ep_e4m3fn_encode(_ptr(v.contiguous(), "f32", "v"), _ptr(out), v.numel(), _stream()))
     return out
 
 
@@ -553,8 +588,8 @@ def rank_routing(topk_idx, num_experts: int, num_partitions: int):
     import torch
     T, K = topk_idx.shape
     part = torch.empty((T, min(K, num_partitions)), dtype=torch.int64, device=topk_idx.device)
-    _check(ep_rank_routing(_ptr(topk_idx.contiguous()), T, K, num_experts, num_partitions,
-                           _ptr(part), _stream()))
+    _check(ep_rank_routing(_ptr(topk_idx.contiguous(), "i64", "topk_idx"), T, K, num_experts,
+                           num_partitions, _ptr(part), _stream()))
     return part
 
 
@@ -573,7 +608,8 @@ def pack_for_ranks(x, topk_idx, topk_weights, num_experts: int, num_partitions: 
     cap = h.c.capacity_rows
     local_idx = torch.full((cap, K), -1, dtype=torch.int64, device=x.device)
     local_w = torch.zeros((cap, K), dtype=torch.float32, device=x.device)
-    _check(ep_pack_metadata(_ptr(topk_idx.contiguous()), _ptr(topk_weights.contiguous()), K,
+    _check(ep_pack_metadata(_ptr(topk_idx.contiguous(), "i64", "topk_idx"),
+                            _ptr(topk_weights.contiguous(), "f32", "topk_weights"), K,
                             num_experts, _ptr(part), h.c, _ptr(local_idx), _ptr(local_w),
                             _stream()))
     return send_x, send_scales, local_idx, local_w, lay, part

@@ -36,8 +36,8 @@ class _Routing:
 class _Dispatch(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, topk_weights, routing, capacity_rows):
-        w = topk_weights.detach() if topk_weights is not None else None
-        recv, _, handle = _dispatch(x.detach(), w, routing.layout, False, capacity_rows)
+        w = topk_weights.detach().contiguous() if topk_weights is not None else None
+        recv, _, handle = _dispatch(x.detach().contiguous(), w, routing.layout, False, capacity_rows)
         routing.handle = handle
         ctx.handle = handle
         return recv
@@ -56,8 +56,8 @@ def _unmapped_rows_zeroed(y, handle):
     c = handle.c
     dense = c.static_cap == 0 and c.expert_alignment <= 1
     if not dense or handle.num_recv is None:
-        return torch.zeros_like(y)
-    grad_y = torch.empty_like(y)
+        return torch.zeros_like(y, memory_format=torch.contiguous_format)
+    grad_y = torch.empty_like(y, memory_format=torch.contiguous_format)
     grad_y[min(handle.num_recv, c.capacity_rows):].zero_()
     return grad_y
 
@@ -65,8 +65,8 @@ def _unmapped_rows_zeroed(y, handle):
 class _Combine(torch.autograd.Function):
     @staticmethod
     def forward(ctx, y, topk_weights, handle):
-        w = topk_weights.detach() if topk_weights is not None else None
-        out = _combine(y.detach(), handle, w)
+        w = topk_weights.detach().contiguous() if topk_weights is not None else None
+        out = _combine(y.detach().contiguous(), handle, w)
         ctx.handle = handle
         ctx.save_for_backward(y, topk_weights)
         return out
@@ -77,8 +77,8 @@ class _Combine(torch.autograd.Function):
         want_w = w is not None and ctx.needs_input_grad[1]
         grad_y = _unmapped_rows_zeroed(y, ctx.handle)
         gy, gw = _combine_backward(grad_out.contiguous(), ctx.handle,
-                                   y=y.detach() if want_w else None,
-                                   topk_weights=w.detach() if w is not None else None,
+                                   y=y.detach().contiguous() if want_w else None,
+                                   topk_weights=w.detach().contiguous() if w is not None else None,
                                    grad_y=grad_y)
         return gy, (gw if want_w else None), None
 

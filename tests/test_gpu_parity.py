@@ -591,3 +591,31 @@ def test_token_owner_form_of_combine(ep, monkeypatch, T, H, K, E, P):
     gx = ep.dispatch_backward(_bf16_tensor(g, dev), got["handle"])
     torch.cuda.synchronize()
     assert np.array_equal(_bits(gx), oracle.dispatch_backward(g[:ref["rows"]], ref["slot"]))
+
+
+def test_binding_refuses_views_wrong_types_and_host_tensors(ep):
+    """The binding hands the library bare addresses of dense rows, so it
+    refuses what would be misread: a non-contiguous view, an element type the
+    call does not take, a tensor in host memory."""
+    dev = _dev()
+    idx, w = workloads.random_case(71, 64, 16, 4)
+    t_idx = torch.from_numpy(idx).to(dev)
+    with pytest.raises(TypeError):
+        ep.get_dispatch_layout(t_idx.to(torch.int32), 16, 4)
+    with pytest.raises(ValueError):
+        ep.get_dispatch_layout(torch.from_numpy(idx), 16, 4)
+    lay = ep.get_dispatch_layout(t_idx, 16, 4)
+    x = torch.randn((256, 64), device=dev).to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        ep.dispatch(x.t(), torch.from_numpy(w).to(dev), lay, False)          # [64, 256] view
+    with pytest.raises(TypeError):
+        ep.dispatch(x.t().contiguous().float(), torch.from_numpy(w).to(dev), lay, False)
+    recv, _, h = ep.dispatch(x.t().contiguous(), torch.from_numpy(w).to(dev), lay, False)
+    y = torch.zeros((recv.shape[0], 256), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(TypeError):
+        ep.combine(y, h, torch.from_numpy(w).to(dev).double())
+    with pytest.raises(ValueError):
+        ep.combine(torch.zeros((256, recv.shape[0]), dtype=torch.bfloat16, device=dev).t(), h)
+    out = ep.combine(y, h)
+    torch.cuda.synchronize()
+    assert out.shape == (64, 256) and not out.view(torch.int16).any()
