@@ -71,7 +71,8 @@ def parse():
     ap.add_argument("--no-ep-share", action="store_true",
                     help="skip the expert-parallel side figure (its pack dispatch shares the main "
                          "dispatch's kernel and grid, so counter runs of the step leave it out)")
-    ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--cpu-runs", type=int, default=6,
+                    help="oracle runs of the whole step for the CPU baseline (median; about 10 s at v3)")
     ap.add_argument("--low-latency", action="store_true",
                     help="one-launch static-capacity dispatch (T <= 256) instead of layout + dispatch")
     ap.add_argument("--ll-cap", type=int, default=0,
