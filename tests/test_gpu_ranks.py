@@ -99,7 +99,7 @@ def _flow(ep, wl_or_case, use_fp8, seed):
     return got, _bits(partials[:n]), _bits(out), ref
 
 
-@pytest.mark.parametrize("name", ["tiny", "skewed", "decode", "v3"])
+@pytest.mark.parametrize("name", ["tiny", "skewed", "decode", "v3", "large"])
 def test_flow_matches_the_oracle(ep, name):
     """Pack -> (identity exchange) -> unpack per destination -> pre-reduce with
     the received weights -> origin sum in rank order, each stage bit-exact."""
