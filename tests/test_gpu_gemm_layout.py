@@ -93,7 +93,7 @@ def _check(ep, lay, h, recv, sc, cap, ref, use_fp8, col_major=False):
 
 @pytest.mark.parametrize("name,A,col_major", [("v3", 128, False), ("v3", 128, True),
                                               ("skewed", 64, False), ("decode", 16, True),
-                                              ("tiny", 4, False)])
+                                              ("tiny", 4, False), ("large", 128, True)])
 def test_aligned_layout_full_workloads(ep, name, A, col_major):
     wl = workloads.config(name)
     idx, w, x = workloads.make(wl)
