@@ -44,7 +44,7 @@ def _codes(rng, shape):
     return q
 
 
-@pytest.mark.parametrize("name", ["decode", "v3"])
+@pytest.mark.parametrize("name", ["decode", "v3", "large"])
 def test_round_trip_from_dispatch(ep, name):
     """dispatch (FP8) -> combine_fp8 (weights) and dispatch_backward_fp8 (unit)
     on the rows and scales dispatch produced."""
