@@ -123,16 +123,24 @@ def _run(ep, idx, w, x, E, P, cap, use_fp8, pass_weights=True):
     return recv, sc, lay, t_w
 
 
-def test_decode_workload_fp8():
-    """The 128-token decode batch (H=7168, 256 experts, top-8, FP8), with a
-    per-expert capacity of 32 rows, then combine through the same handle."""
+@pytest.mark.parametrize("name,cap", [("decode", 32), ("tiny", 12)])
+def test_small_workloads(name, cap):
+    """The two batches of at most 256 tokens through the one-launch dispatch,
+    then combine through the same handle: decode (H=7168, 256 experts,
+    top-8, FP8) with 32 rows per expert, nothing dropped; tiny (H=256, 16
+    experts, top-2, BF16) with 12 rows per expert, so the most popular
+    experts drop pairs."""
     ep = pytest.importorskip("combine_get_dispatch_scan_amd")
-    wl = workloads.config("decode")
+    wl = workloads.config(name)
     idx, w, x = workloads.make(wl)
-    cap = 32
-    recv, sc, lay, t_w = _run(ep, idx, w, x, wl.E, wl.P, cap, True)
-    ref = _check_dispatch(ep, idx, w, x, wl.E, wl.P, cap, True, recv, sc, lay)
-    assert ref["overflow"] == 0
+    recv, sc, lay, t_w = _run(ep, idx, w, x, wl.E, wl.P, cap, wl.use_fp8)
+    ref = _check_dispatch(ep, idx, w, x, wl.E, wl.P, cap, wl.use_fp8, recv, sc, lay)
+    counts = np.bincount(idx[idx >= 0], minlength=wl.E)
+    assert ref["overflow"] == int(counts.max() > cap)
+    if name == "decode":
+        assert ref["overflow"] == 0
+    else:
+        assert ref["overflow"] == 1
     y = workloads.expert_outputs(wl, wl.E * cap)
     out = ep.combine(_bf16(y, _dev()), lay.handle)
     np.testing.assert_array_equal(_bits(out), oracle.combine(y, ref["slot"], w))
