@@ -64,6 +64,14 @@ MUTANTS = [
     ("static slots: row off by one",
      "slot[i] = (int32_t)e * cap + r;", "slot[i] = (int32_t)e * cap + r + (r + 1 < cap);",
      [lambda: pins.test_static_slots_against_stable_sort(128, 256, 8, 16, "clean")]),
+    ("FP8 input: scales of the previous token",
+     "memcpy(scales + (size_t)r * nb, xs + (size_t)t * nb, sizeof(float) * (size_t)nb);",
+     "memcpy(scales + (size_t)r * nb, xs + (size_t)(t > 0 ? t - 1 : 0) * nb, sizeof(float) * (size_t)nb);",
+     [pins.test_fp8_input_dispatch_copies_codes_and_scales]),
+    ("FP8 input: codes of the mirrored token",
+     "memcpy(recv + (size_t)r * H, xq + (size_t)t * H, (size_t)H);",
+     "memcpy(recv + (size_t)r * H, xq + (size_t)(T - 1 - t) * H, (size_t)H);",
+     [pins.test_fp8_input_dispatch_copies_codes_and_scales]),
     ("dispatch: only the first block's scale copied",
      "memcpy(scales + (size_t)r * nb, s, sizeof(float) * (size_t)nb);",
      "memcpy(scales + (size_t)r * nb, s, sizeof(float));",
