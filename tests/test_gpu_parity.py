@@ -619,3 +619,51 @@ def test_binding_refuses_views_wrong_types_and_host_tensors(ep):
     out = ep.combine(y, h)
     torch.cuda.synchronize()
     assert out.shape == (64, 256) and not out.view(torch.int16).any()
+
+
+def _random_cases(n=40, seed=2026):
+    """Seeded shapes across the boundary's range: T up to 3000 (0 included),
+    K up to 16, E up to 1024 in P up to 64 partitions, hidden sizes on and
+    off the row steps, clean and dirty ids, full and reduced capacities."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        P = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        E = P * int(rng.integers(1, 1024 // P + 1))
+        K = int(rng.integers(1, 17))
+        T = 0 if i == 0 else int(np.exp(rng.uniform(0, np.log(3000))))
+        fp8 = bool(rng.integers(0, 2))
+        H = 128 * int(rng.integers(1, 25)) if fp8 else 8 * int(rng.integers(1, 601))
+        dirty = bool(rng.integers(0, 2))
+        cap_frac = float(rng.choice([1.0, 1.0, rng.uniform(0, 1)]))
+        cases.append((i, T, H, E, K, P, fp8, dirty, cap_frac))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "case%d" % c[0])
+def test_random_shapes(ep, case):
+    """Layout, slots, rows, scales and combine bit-exact, then both backward
+    calls on the same handle, on seeded random shapes."""
+    i, T, H, E, K, P, fp8, dirty, cap_frac = case
+    kw = dict(distinct=K <= E and not dirty)
+    if dirty:
+        kw.update(mask_frac=0.1, invalid_frac=0.03, dup_frac=0.05)
+    idx, w = workloads.random_case(5000 + i, T, E, K, **kw)
+    x = workloads.random_rows(6000 + i, T, H, "normal")
+    cap = None if cap_frac >= 1.0 else int(T * K * cap_frac)
+    ref, got = check(ep, idx, w, x, E, P, fp8, capacity=cap, tag=f"random-{i}")
+    if T == 0:
+        return
+    dev = _dev()
+    h = got["handle"]
+    rows_cap = T * K if cap is None else cap
+    gr = workloads.random_rows(7000 + i, rows_cap, H, "normal")
+    g = workloads.random_rows(8000 + i, T, H, "normal")
+    gx = ep.dispatch_backward(_bf16_tensor(gr, dev) if rows_cap else
+                              torch.empty((0, H), dtype=torch.bfloat16, device=dev), h)
+    gy, _ = ep.combine_backward(_bf16_tensor(g, dev), h)
+    torch.cuda.synchronize()
+    rows = ref["rows"]
+    assert np.array_equal(_bits(gx), oracle.dispatch_backward(gr[:rows], ref["slot"]))
+    ref_gy, _ = oracle.combine_backward(g, None, ref["slot"], w, rows_cap)
+    assert np.array_equal(_bits(gy)[:rows], ref_gy[:rows])
