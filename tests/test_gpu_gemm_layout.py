@@ -72,7 +72,8 @@ def _check(ep, lay, h, recv, sc, cap, ref, use_fp8, col_major=False):
     counts, n, status = ep.handle_recv_counts(h)
     np.testing.assert_array_equal(np.array(counts), np.diff(ref["expert_offset"]))
     assert n == int(ref["expert_offset"][-1])
-    assert status == (ep.EP_ECAPACITY if ref["overflow"] else ep.EP_OK)
+    assert status == (ep.EP_ECAPACITY if ref["overflow"] else
+                      (ep.EP_EIDS if ref["num_invalid"] else ep.EP_OK))
     rows = ref["rows"]
     got = recv.cpu().numpy()
     if use_fp8:

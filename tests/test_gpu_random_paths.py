@@ -1,0 +1,129 @@
+"""Seeded random shapes through the paths beside the dense forward, each
+against the CPU oracle: the one-launch low-latency dispatch (then combine on
+its static handle), GEMM-aligned layouts (column-major scales and FP8 input
+included), and the expert-parallel flow over ranks.  Bit-exact throughout."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+import test_gpu_gemm_layout as gl
+import test_gpu_low_latency as ll
+import test_gpu_ranks as rk
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _routing(rng, E_max=1024):
+    P = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    E = P * int(rng.integers(1, max(1, E_max // P) + 1))
+    K = int(rng.integers(1, 17))
+    return E, K, P
+
+
+def _ids(seed, T, E, K, dirty):
+    kw = dict(distinct=K <= E and not dirty)
+    if dirty:
+        kw.update(mask_frac=0.1, invalid_frac=0.03, dup_frac=0.05)
+    return workloads.random_case(seed, T, E, K, **kw)
+
+
+def _ll_cases(n=15, seed=11):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E, K, P = _routing(rng)
+        T = 0 if i == 0 else int(rng.integers(1, 257))
+        fp8 = bool(rng.integers(0, 2))
+        H = 128 * int(rng.integers(1, 17)) if fp8 else 8 * int(rng.integers(1, 401))
+        cap = int(rng.integers(1, 65))
+        out.append((i, T, H, E, K, P, fp8, bool(rng.integers(0, 2)), cap))
+    return out
+
+
+@pytest.mark.parametrize("case", _ll_cases(), ids=lambda c: "ll%d" % c[0])
+def test_low_latency_random(ep, case):
+    i, T, H, E, K, P, fp8, dirty, cap = case
+    print(f"[random] low-latency {case}", flush=True)
+    idx, w = _ids(9100 + i, T, E, K, dirty)
+    x = workloads.random_rows(9200 + i, T, H, "normal")
+    recv, sc, lay, t_w = ll._run(ep, idx, w, x, E, P, cap, fp8)
+    ref = ll._check_dispatch(ep, idx, w, x, E, P, cap, fp8, recv, sc, lay)
+    if T == 0:
+        return
+    y = workloads.random_rows(9300 + i, E * cap, H, "normal")
+    out = ep.combine(ll._bf16(y, ll._dev()), lay.handle)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ll._bits(out), oracle.combine(y, ref["slot"], w))
+
+
+def _aligned_cases(n=15, seed=12):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E, K, P = _routing(rng, E_max=256)
+        T = int(rng.integers(1, 2001))
+        fp8 = bool(rng.integers(0, 2))
+        H = 128 * int(rng.integers(1, 17)) if fp8 else 8 * int(rng.integers(1, 257))
+        A = int(rng.choice([2, 3, 16, 64, 128]))
+        A = max(2, min(A, 1 + 32768 // E))              # at most 32768 padding rows
+        col_major = fp8 and bool(rng.integers(0, 2))
+        fp8_input = fp8 and bool(rng.integers(0, 2))
+        out.append((i, T, H, E, K, P, fp8, bool(rng.integers(0, 2)), A, col_major, fp8_input))
+    return out
+
+
+@pytest.mark.parametrize("case", _aligned_cases(), ids=lambda c: "aligned%d" % c[0])
+def test_aligned_layout_random(ep, case):
+    i, T, H, E, K, P, fp8, dirty, A, col_major, fp8_input = case
+    print(f"[random] aligned {case}", flush=True)
+    idx, w = _ids(9400 + i, T, E, K, dirty)
+    if fp8_input:
+        rng = np.random.default_rng(9500 + i)
+        xq = rng.integers(0, 256, (T, H), dtype=np.uint32).astype(np.uint8)
+        xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+        lay, h, recv, sc, cap, _, _ = gl._run(ep, idx, w, xq, E, P, A, True, x_scales=xs,
+                                              col_major=col_major)
+        ref = oracle.run_all(idx, w, None, E, P, True, align=A)
+        q, s = oracle.dispatch_fp8_input(xq, xs, ref["slot"], ref["rows"])
+        ref.update(recv_x=q, recv_scales=s)
+    else:
+        x = workloads.random_rows(9600 + i, T, H, "normal")
+        lay, h, recv, sc, cap, _, _ = gl._run(ep, idx, w, x, E, P, A, fp8, col_major=col_major)
+        ref = oracle.run_all(idx, w, x, E, P, fp8, align=A)
+    gl._check(ep, lay, h, recv, sc, cap, ref, fp8, col_major)
+    # combine through the aligned handle: padding rows are never gathered
+    y = workloads.random_rows(9700 + i, cap, H, "normal")
+    out = ep.combine(gl._bf16(y, gl._dev()), h)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gl._bits(out), oracle.combine(y, ref["slot"], w))
+
+
+def _ranks_cases(n=15, seed=13):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E, K, P = _routing(rng, E_max=512)
+        T = int(rng.integers(1, 1501))
+        fp8 = bool(rng.integers(0, 2))
+        H = 128 * int(rng.integers(1, 17)) if fp8 else 8 * int(rng.integers(1, 257))
+        out.append((i, T, H, E, K, P, fp8, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _ranks_cases(), ids=lambda c: "ranks%d" % c[0])
+def test_rank_flow_random(ep, case):
+    i, T, H, E, K, P, fp8, dirty = case
+    print(f"[random] ranks {case}", flush=True)
+    idx, w = _ids(9800 + i, T, E, K, dirty)
+    x = workloads.random_rows(9900 + i, T, H, "normal")
+    got, partials, out, ref = rk._flow(ep, (idx, w, x, E, P), fp8, 10000 + 100 * i)
+    for p, (g, d) in enumerate(zip(got, ref["dest"])):
+        u = d["unpack"]
+        assert g["n"] == u["rows"], p
+        assert np.array_equal(g["slot"], u["slot"]), p
+        assert np.array_equal(g["rows"], u["recv_x"][:u["rows"]]), p
+    assert np.array_equal(partials, ref["partials"])
+    assert np.array_equal(out, ref["out"])
