@@ -659,11 +659,17 @@ def test_random_shapes(ep, case):
     rows_cap = T * K if cap is None else cap
     gr = workloads.random_rows(7000 + i, rows_cap, H, "normal")
     g = workloads.random_rows(8000 + i, T, H, "normal")
-    gx = ep.dispatch_backward(_bf16_tensor(gr, dev) if rows_cap else
-                              torch.empty((0, H), dtype=torch.bfloat16, device=dev), h)
-    gy, _ = ep.combine_backward(_bf16_tensor(g, dev), h)
+    empty = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    gx = ep.dispatch_backward(_bf16_tensor(gr, dev) if rows_cap else empty, h)
+    yb = workloads.random_rows(9000 + i, rows_cap, H, "normal")
+    gy, gw = ep.combine_backward(_bf16_tensor(g, dev), h, y=_bf16_tensor(yb, dev) if rows_cap else empty)
     torch.cuda.synchronize()
     rows = ref["rows"]
     assert np.array_equal(_bits(gx), oracle.dispatch_backward(gr[:rows], ref["slot"]))
-    ref_gy, _ = oracle.combine_backward(g, None, ref["slot"], w, rows_cap)
+    ref_gy, ref_gw = oracle.combine_backward(g, yb[:rows], ref["slot"], w, rows_cap)
     assert np.array_equal(_bits(gy)[:rows], ref_gy[:rows])
+    if rows_cap == 0:
+        assert not gw.cpu().numpy().any()           # nothing dispatched: every grad_w is 0
+    else:
+        from test_gpu_backward import _check_grad_w_all
+        _check_grad_w_all(gw.cpu().numpy(), ref_gw, g, yb, ref["slot"], H)
