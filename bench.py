@@ -458,6 +458,46 @@ def measure_low_latency(config, ll_cap, steps, warmup):
     copy_gbps = (2 << 30) / (batch_us(lambda: dst.copy_(src), 5) * 1e-6) / 1e9
     fill_gbps = (1 << 30) / (batch_us(lambda: dst.fill_(3), 5) * 1e-6) / 1e9
     del src, dst
+    # floors at this size, timed like the dispatch: each call launched 50
+    # times inside one captured HIP graph (no host work between launches),
+    # per-launch time from two events around a replay.  A fill of 4 bytes
+    # is launch and completion alone; a fill of as many bytes as the
+    # dispatch writes adds the writes.  int32 fills are kernels (no memset
+    # node in the graph).
+    def graph_us(fn, n=50):
+        side_s = torch.cuda.Stream()
+        side_s.wait_stream(stream)
+        with torch.cuda.stream(side_s):
+            fn()
+        stream.wait_stream(side_s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(n):
+                fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        gr.replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / n
+    b_row = 1 if wl.use_fp8 else 2
+    written = N * (H * b_row + (4 * (H // 128) if wl.use_fp8 else 0)) + T * K * 8 + T * P
+    wbuf = torch.empty((written + 3) // 4, dtype=torch.int32, device=dev)
+    tiny = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def ll_only():
+        if ep.ep_low_latency_dispatch(*ll_args[:-1], ep._stream()):
+            raise RuntimeError(ep.ep_last_error())
+    floors = {"protocol": "50 launches in one captured graph, per launch",
+              "low_latency_dispatch": round(graph_us(ll_only), 2),
+              "fill_of_the_written_bytes": round(graph_us(lambda: wbuf.fill_(7)), 2),
+              "fill_of_4_bytes": round(graph_us(lambda: tiny.fill_(7)), 2),
+              "written_bytes": written}
+    del wbuf, tiny
 
     # the same forward captured once and replayed (no host work per step)
     side = torch.cuda.Stream()
@@ -504,6 +544,7 @@ def measure_low_latency(config, ll_cap, steps, warmup):
         "graph_replay_us_per_step": round(graph_ms * 1e3, 2),
         "kernels_us": {"low_latency_dispatch": round(disp_us, 2), "combine": round(comb_us, 2)},
         "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},
+        "latency_floors_us": floors,
         "roofline": {"bound": "hbm", "kernel": "low_latency_dispatch_kernel",
                      "achieved": round(disp_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(disp_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": disp_alg,
@@ -866,7 +907,7 @@ def main():
             "us_per_step": round(ll["ms_per_step"] * 1e3, 2),
             "us_per_step_stats": ll["us_per_step_stats"],
             "graph_replay_us_per_step": ll["graph_replay_us_per_step"], "kernels_us": ll["kernels_us"],
-            "dispatch_roofline_frac": ll["roofline"]["frac"]}
+            "dispatch_roofline_frac": ll["roofline"]["frac"], "latency_floors_us": ll["latency_floors_us"]}
 
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_runs} oracle runs)", file=sys.stderr, flush=True)
