@@ -154,6 +154,54 @@ def cpu_baseline(wl, idx, w, x, y, runs):
     return statistics.median(times), r["N"], r
 
 
+def cpu_side_figures(wl, idx, w, x, y, ref):
+    """Part of the CPU-baseline leg: the oracle, single thread, one run per
+    call, on the inputs of the side figures (ref: the oracle's run of the
+    step, slots and combine output included).  Seconds per call."""
+    import oracle
+    T, K = idx.shape
+    H = x.shape[1]
+    slot = ref["slot"]
+
+    def secs(fn):
+        t0 = time.perf_counter()
+        fn()
+        return round(time.perf_counter() - t0, 3)
+    res = {"backward": {"dispatch_backward": secs(lambda: oracle.dispatch_backward(y, slot)),
+                        "combine_backward_with_grad_w":
+                            secs(lambda: oracle.combine_backward(ref["out"], y, slot, w, T * K))}}
+    if wl.use_fp8:
+        res["backward"]["dispatch_backward_fp8"] = secs(
+            lambda: oracle.combine_fp8(ref["recv_x"], ref["recv_scales"], slot, None))
+        xq = np.random.default_rng(1).integers(0, 256, (T, H), dtype=np.uint8)
+        xs = np.ones((T, H // 128), np.float32)
+        res["gemm_layout"] = {
+            "aligned128_layout_and_dispatch": secs(lambda: oracle.run_all(idx, w, x, wl.E, wl.P, True, align=128)),
+            "fp8_input_dispatch": secs(lambda: oracle.dispatch_fp8_input(xq, xs, slot, ref["rows"]))}
+        # the expert-parallel flow: one untimed run sizes the expert outputs
+        sizing = oracle.ep_one_source(idx, w, x, wl.E, wl.P, True)
+        y_parts = [np.zeros((d["unpack"]["rows"], H), np.uint16) + np.uint16(0x3F80)
+                   for d in sizing["dest"]]
+        res["ep_rank_share"] = {"whole_flow": secs(
+            lambda: oracle.ep_one_source(idx, w, x, wl.E, wl.P, True, y_parts=y_parts))}
+    return res
+
+
+def cpu_decode_figure():
+    """Part of the CPU-baseline leg: the oracle's one-launch-equivalent
+    decode step (static-capacity layout, slots and FP8 rows, then combine),
+    single thread, at the decode shape with cap = T rows per expert."""
+    import oracle
+    import workloads
+    wl = workloads.config("decode")
+    idx, w, x = workloads.make(wl)
+    y = workloads.expert_outputs(wl, wl.E * wl.T)
+    t0 = time.perf_counter()
+    r = oracle.run_low_latency(idx, w, x, wl.E, wl.P, wl.use_fp8, wl.T)
+    oracle.combine(y, r["slot"], w)
+    return round(time.perf_counter() - t0, 4)
+
+
 def cpu_model():
     """The host CPU's model name, read at run time."""
     try:
@@ -915,6 +963,14 @@ def main():
         assert n_cpu == N
         res["parity"] = parity_verdict(gpu_out, ref, N, wl.use_fp8)
         print(f"[bench] parity: {res['parity']}", file=sys.stderr, flush=True)
+        print("[bench] cpu oracle beside the side figures", file=sys.stderr, flush=True)
+        side = cpu_side_figures(wl, idx, w, x, y, ref)
+        for key, secs_map in side.items():
+            if res.get(key):
+                res[key]["cpu_oracle_s"] = dict(secs_map, note="the oracle, one thread, one run per call")
+        if res.get("low_latency_decode"):
+            res["low_latency_decode"]["cpu_oracle_s"] = {"step": cpu_decode_figure(),
+                                                         "note": "the oracle, one thread, one run"}
         nthr = host_threads()
         print(f"[bench] cpu baseline, {nthr} threads", file=sys.stderr, flush=True)
         sec_mt, same_mt = cpu_baseline_threaded(wl, idx, w, x, y, args.cpu_runs, nthr, ref)

@@ -136,3 +136,25 @@ def test_default_step_counts_follow_the_launch_bound_rule():
     assert bench.default_steps("tiny") == 1000 and bench.default_steps("decode") == 1000
     for name in ("v3", "skewed", "large"):
         assert bench.default_steps(name) == 100
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_oracle_timings_beside_the_side_figures(name):
+    """The CPU-baseline leg times the oracle on each side figure's inputs:
+    the backward calls always, the GEMM-facing dispatches and the
+    expert-parallel flow in FP8 mode."""
+    wl = workloads.config(name)
+    idx, w, x = workloads.make(wl)
+    N = int((idx >= 0).sum())
+    y = workloads.expert_outputs(wl, N)
+    _, _, ref = bench.cpu_baseline(wl, idx, w, x, y, 1)
+    side = bench.cpu_side_figures(wl, idx, w, x, y, ref)
+    assert set(side["backward"]) >= {"dispatch_backward", "combine_backward_with_grad_w"}
+    if wl.use_fp8:
+        assert "dispatch_backward_fp8" in side["backward"]
+        assert set(side["gemm_layout"]) == {"aligned128_layout_and_dispatch", "fp8_input_dispatch"}
+        assert "whole_flow" in side["ep_rank_share"]
+    else:
+        assert set(side) == {"backward"}
+    assert all(v >= 0 for d in side.values() for v in d.values())
+    assert bench.cpu_decode_figure() > 0
