@@ -75,6 +75,9 @@ extern "C" {
  * device arrays it points to live inside the caller's workspace and stay valid
  * while that workspace is neither freed nor reused by another layout call.
  * Treat the fields as read-only.
+ * Calls that take a handle refuse, with EP_EINVAL, one the layout call did
+ * not fill (magic), one below the stage the call needs, and one whose
+ * dimensions are outside the limits above.
  */
 typedef struct ep_handle {
     uint32_t magic;            /* EP_HANDLE_MAGIC once the layout call filled it  */
@@ -116,7 +119,7 @@ typedef struct ep_handle {
 
 /* Library version, major*10000 + minor*100 + patch.  EP_VERSION is the
  * version of this header; ep_version() that of the loaded library. */
-#define EP_VERSION 10200
+#define EP_VERSION 10201
 int ep_version(void);
 
 /* Message describing the last error returned on this thread ("" if none). */
