@@ -32,6 +32,9 @@
  *    scale = a / 448 (fp32, dequantise as code * scale).
  *  - combine accumulates in fp32 with one fused multiply-add per dispatched k
  *    in ascending k from +0.0f, then rounds to BF16 (nearest even).
+ *  - x, y, the gradients and the weights are finite.  NaN and infinities are
+ *    outside the contract: the codes, scales and sums they touch are then
+ *    unspecified (no call traps or faults on them).
  *  - Limits: 1 <= K <= 16, 1 <= E <= 1024, 1 <= P <= 64, E % P == 0,
  *    0 <= T, T*K < 2^31, 1 <= H <= 32768, H % 8 == 0 (H % 128 == 0 for FP8).
  *    x, recv_x, y and out must be 16-byte aligned, topk_idx 8-byte, the other
