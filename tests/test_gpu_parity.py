@@ -673,3 +673,30 @@ def test_random_shapes(ep, case):
     else:
         from test_gpu_backward import _check_grad_w_all
         _check_grad_w_all(gw.cpu().numpy(), ref_gw, g, yb, ref["slot"], H)
+
+
+def test_debug_launch_trace():
+    """EP_DEBUG=1 makes every launch print its kernel, grid, block and LDS
+    (read once per process, so a child process runs a small forward)."""
+    import os
+    import subprocess
+    import sys
+    _dev()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import torch, combine_get_dispatch_scan_amd as ep\n"
+        "d = torch.device('cuda:0')\n"
+        "idx = torch.randint(0, 32, (600, 4), device=d)\n"
+        "lay = ep.get_dispatch_layout(idx, 32, 4)\n"
+        "x = torch.randn((600, 256), device=d).to(torch.bfloat16)\n"
+        "recv, sc, h = ep.dispatch(x, torch.rand((600, 4), device=d), lay, True)\n"
+        "ep.combine(torch.zeros((recv.shape[0], 256), dtype=torch.bfloat16, device=d), h)\n"
+        "torch.cuda.synchronize()\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, EP_DEBUG="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[moe_ep] ")]
+    kernels = [l.split()[1] for l in lines]
+    assert kernels[:4] == ["layout_chunk_kernel", "scan_kernel", "dispatch_fp8_kernel", "combine_kernel"], lines
+    assert all("grid=(" in l and "block=(" in l and "lds=" in l for l in lines)
