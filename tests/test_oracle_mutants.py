@@ -122,19 +122,19 @@ MUTANTS = [
     ("rank routing: destinations in descending order",
      "        for (int p = 0; p < P; ++p)\n            if (hit[p])",
      "        for (int p = P - 1; p >= 0; --p)\n            if (hit[p])",
-     [lambda: pins.test_rank_routing_against_brute_force(50, 16, 4, 4, "clean")]),
+     [lambda: pins.test_rank_routing_against_brute_force(50, 16, 4, 4, "clean"), pins.test_ep_worked_example]),
     ("pack metadata: local id not offset by the partition's first expert",
      "local_idx[(size_t)r * K + k] = local ? e - p * epp : -1;",
      "local_idx[(size_t)r * K + k] = local ? e - p : -1;",
-     [lambda: pins.test_pack_metadata_against_brute_force(50, 16, 4, 4, "clean")]),
+     [lambda: pins.test_pack_metadata_against_brute_force(50, 16, 4, 4, "clean"), pins.test_ep_worked_example]),
     ("pack metadata: weights of experts elsewhere not zeroed",
      "local_w[(size_t)r * K + k] = local ? topk_weights[(size_t)t * K + k] : 0.0f;",
      "local_w[(size_t)r * K + k] = topk_weights[(size_t)t * K + k];",
-     [lambda: pins.test_pack_metadata_against_brute_force(50, 16, 4, 4, "clean")]),
+     [lambda: pins.test_pack_metadata_against_brute_force(50, 16, 4, 4, "clean"), pins.test_ep_worked_example]),
     ("pack metadata: repeated ids taken as local",
      "int local = ok[k] && e / epp == p;",
      "int local = e >= 0 && e < E && e / epp == p;",
-     [lambda: pins.test_pack_metadata_against_brute_force(200, 64, 6, 8, "dirty")]),
+     [lambda: pins.test_pack_metadata_against_brute_force(200, 64, 6, 8, "dirty"), pins.test_ep_worked_example]),
 ]
 
 

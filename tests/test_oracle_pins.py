@@ -236,6 +236,34 @@ def test_layout_worked_example():
     assert np.array_equal(_f32(out), np.array(cb["out"], np.float32))
 
 
+
+def test_ep_worked_example():
+    """The expert-parallel flow on the hand-worked example in
+    golden/ep_worked_example.json: destinations, packed rows and their
+    metadata, each destination's receive rows, pre-reduced rows and the
+    origin's sums, every value given there."""
+    g = json.load(open(os.path.join(GOLDEN, "ep_worked_example.json")))
+    idx = np.array(g["topk_idx"], np.int64)
+    w = np.array(g["topk_weights"], np.float32)
+    E, P, H = g["E"], g["P"], g["H"]
+    x = workloads.bf16_bits_from_f32(np.arange(g["T"] * H, dtype=np.float32).reshape(g["T"], H))
+    y_parts = [workloads.bf16_bits_from_f32(np.array([[10 * p + u + 1, -(10 * p + u + 1)] for u in range(n)],
+                                                     np.float32).reshape(n, H))
+               for p, n in enumerate(g["expert_outputs"]["rows_per_destination"])]
+    r = oracle.ep_one_source(idx, w, x, E, P, False, y_parts=y_parts)
+    assert r["part_idx"].tolist() == g["part_idx"]
+    assert r["pack"]["num_tokens_per_expert"].tolist() == g["pack_rows_per_destination"]
+    assert r["pack"]["slot"].tolist() == g["pack_slot"]
+    rows = sum(g["pack_rows_per_destination"])
+    assert r["local_idx"][:rows].tolist() == g["local_idx"]
+    assert np.array_equal(r["local_w"][:rows], np.array(g["local_w"], np.float32))
+    for p, d in enumerate(r["dest"]):
+        assert d["unpack"]["slot"].tolist() == g["unpack_slot"][p], p
+        assert d["unpack"]["rows"] == g["expert_outputs"]["rows_per_destination"][p], p
+    assert np.array_equal(_f32(r["partials"]), np.array(g["partials"], np.float32))
+    assert np.array_equal(_f32(r["out"]), np.array(g["out"], np.float32))
+
+
 CASES = [
     dict(T=1, E=1, K=1, P=1), dict(T=7, E=8, K=3, P=2), dict(T=64, E=16, K=4, P=4),
     dict(T=65, E=32, K=8, P=8), dict(T=300, E=64, K=6, P=8), dict(T=513, E=256, K=8, P=16),
