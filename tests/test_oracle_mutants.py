@@ -54,7 +54,7 @@ MUTANTS = [
      [lambda: pins.test_layout_and_slots_against_independent_definitions(C[2], "clean")]),
     ("aligned offsets: rounded down",
      "off[e + 1] = off[e] + ((c + A - 1) / A) * A;", "off[e + 1] = off[e] + (c / A) * A;",
-     [lambda: pins.test_aligned_offsets_closed_form(64)]),
+     [lambda: pins.test_aligned_offsets_closed_form(64), pins.test_layout_worked_example]),
     ("slots: wrong source token",
      "src_token[s] = t;", "src_token[s] = t > 0 ? t - 1 : 0;",
      [lambda: pins.test_layout_and_slots_against_independent_definitions(C[2], "clean")]),
@@ -63,7 +63,7 @@ MUTANTS = [
      [pins.test_dispatch_capacity_drops_rows]),
     ("static slots: row off by one",
      "slot[i] = (int32_t)e * cap + r;", "slot[i] = (int32_t)e * cap + r + (r + 1 < cap);",
-     [lambda: pins.test_static_slots_against_stable_sort(128, 256, 8, 16, "clean")]),
+     [lambda: pins.test_static_slots_against_stable_sort(128, 256, 8, 16, "clean"), pins.test_layout_worked_example]),
     ("FP8 input: scales of the previous token",
      "memcpy(scales + (size_t)r * nb, xs + (size_t)t * nb, sizeof(float) * (size_t)nb);",
      "memcpy(scales + (size_t)r * nb, xs + (size_t)(t > 0 ? t - 1 : 0) * nb, sizeof(float) * (size_t)nb);",

@@ -234,6 +234,15 @@ def test_layout_worked_example():
     y = np.array([[r, -r] for r in range(9)], np.float32)
     out = oracle.combine(workloads.bf16_bits_from_f32(y), slot, np.array(cb["weights"], np.float32))
     assert np.array_equal(_f32(out), np.array(cb["out"], np.float32))
+    al = g["aligned_2"]
+    off2 = oracle.expert_offsets(lay["num_tokens_per_expert"], 2)
+    assert off2.tolist() == al["expert_offset"]
+    slot2, src2, ovf2 = oracle.slots(idx, lay["valid"], off2, int(off2[-1]))
+    assert slot2.tolist() == al["slot"] and ovf2 == 0
+    assert sorted(set(range(int(off2[-1]))) - set(slot2[slot2 >= 0].tolist())) == al["padding_rows"]
+    st = g["static_cap_2"]
+    slot_s, ovf_s = oracle.slots_static(idx, lay["valid"], g["E"], 2)
+    assert slot_s.tolist() == st["slot"] and ovf_s == st["overflow"]
 
 
 
