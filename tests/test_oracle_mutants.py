@@ -90,15 +90,15 @@ MUTANTS = [
     ("dispatch backward: running sum dropped",
      "acc = acc + oracle_bf16_to_f32(grad_recv[(size_t)r * H + j]);",
      "acc = oracle_bf16_to_f32(grad_recv[(size_t)r * H + j]);",
-     [lambda: pins.test_dispatch_backward_is_the_adjoint_of_dispatch(33, 8, 3, 2, 16)]),
+     [lambda: pins.test_dispatch_backward_is_the_adjoint_of_dispatch(33, 8, 3, 2, 16), pins.test_layout_worked_example]),
     ("combine backward: weight dropped from grad_y",
      "grad_y[(size_t)r * H + j] = oracle_bf16_rne(wk * oracle_bf16_to_f32(g[j]));",
      "grad_y[(size_t)r * H + j] = oracle_bf16_rne(oracle_bf16_to_f32(g[j]));",
-     [lambda: pins.test_combine_backward_grad_y_is_the_adjoint_of_combine(40, 8, 3, 2, 16)]),
+     [lambda: pins.test_combine_backward_grad_y_is_the_adjoint_of_combine(40, 8, 3, 2, 16), pins.test_layout_worked_example]),
     ("combine backward: grad_w from the weight instead of y",
      "(double)oracle_bf16_to_f32(y[(size_t)r * H + j]);",
      "(double)wk;",
-     [pins.test_combine_backward_grad_w_matches_finite_differences]),
+     [pins.test_combine_backward_grad_w_matches_finite_differences, pins.test_layout_worked_example]),
     ("dispatch backward: k loop reversed",
      "            for (int k = 0; k < K; ++k) {\n                int32_t r = slot[(size_t)t * K + k];\n"
      "                if (r < 0)\n                    continue;\n                acc = acc + oracle_bf16_to_f32(grad_recv",

@@ -243,6 +243,14 @@ def test_layout_worked_example():
     st = g["static_cap_2"]
     slot_s, ovf_s = oracle.slots_static(idx, lay["valid"], g["E"], 2)
     assert slot_s.tolist() == st["slot"] and ovf_s == st["overflow"]
+    bw = g["backward"]
+    yb = workloads.bf16_bits_from_f32(y)
+    gx = oracle.dispatch_backward(yb, slot)
+    assert np.array_equal(_f32(gx), np.array(bw["dispatch_backward"], np.float32))
+    go = workloads.bf16_bits_from_f32(np.tile(np.array([[1.0, 2.0]], np.float32), (g["T"], 1)))
+    gy, gw = oracle.combine_backward(go, yb, slot, np.array(cb["weights"], np.float32), 9)
+    assert np.array_equal(_f32(gy), np.array(bw["grad_y"], np.float32))
+    assert np.array_equal(gw, np.array(bw["grad_w"], np.float32))
 
 
 
