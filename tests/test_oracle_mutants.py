@@ -22,10 +22,10 @@ MUTANTS = [
     ("e4m3: saturates to the NaN code",
      "return sign | 0x7E;                 /* satfinite: +-448            */",
      "return sign | 0x7F;",
-     [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest]),
+     [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest, pins.test_quant_block_hand_values]),
     ("e4m3: truncates instead of rounding",
      "double n = nearbyint(a / quantum);", "double n = floor(a / quantum);",
-     [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest]),
+     [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest, pins.test_quant_block_hand_values]),
     ("e4m3: subnormal range boundary off by one binade",
      "    if (lead < -6)\n        lead = -6;", "    if (lead < -7)\n        lead = -7;",
      [pins.test_e4m3fn_hand_values, pins.test_e4m3fn_matches_brute_force_nearest]),
@@ -34,10 +34,10 @@ MUTANTS = [
      [pins.test_e4m3fn_decode_roundtrip_and_bound]),
     ("quantisation: inverse scale transposed",
      "float inv = 448.0f / a;", "float inv = a / 448.0f;",
-     [lambda: pins.test_quant_block_properties("normal"), pins.test_quant_block_special_cases]),
+     [lambda: pins.test_quant_block_properties("normal"), pins.test_quant_block_special_cases, pins.test_quant_block_hand_values]),
     ("quantisation: scale inverted",
      "float s = a / 448.0f;", "float s = 448.0f / a;",
-     [lambda: pins.test_quant_block_properties("normal"), pins.test_quant_block_special_cases]),
+     [lambda: pins.test_quant_block_properties("normal"), pins.test_quant_block_special_cases, pins.test_quant_block_hand_values]),
     ("layout: repeated ids not rejected",
      "} else if (e >= E || seen[e]) {", "} else if (e >= E) {",
      [lambda: pins.test_layout_and_slots_against_independent_definitions(C[3], "dirty")]),

@@ -79,6 +79,23 @@ def test_e4m3fn_hand_values():
         assert oracle.e4m3fn(np.float32(v)) == int(code, 16), (v, code)
 
 
+def test_quant_block_hand_values():
+    """Whole 128-channel blocks quantised by hand (golden/e4m3fn_values.json,
+    "blocks"): the block's amax sets one inverse scale for every element."""
+    g = json.load(open(os.path.join(GOLDEN, "e4m3fn_values.json")))["blocks"]
+    for case in g["cases"]:
+        v = np.zeros(128, np.float32)
+        for j, val in case["values"].items():
+            v[int(j)] = val
+        codes, scale = oracle.quant_block(workloads.bf16_bits_from_f32(v))
+        want = np.zeros(128, np.uint8)
+        for j, c in case["codes"].items():
+            want[int(j)] = int(c, 16)
+        assert np.array_equal(np.asarray(codes, np.uint8), want), case
+        if "scale" in case:
+            assert np.float32(scale) == np.float32(case["scale"])
+
+
 def test_e4m3fn_matches_brute_force_nearest():
     rng = np.random.default_rng(5)
     tv, _ = _e4m3_table()
