@@ -86,7 +86,7 @@ MUTANTS = [
      [pins.test_combine_pow2_weights_exact, pins.test_combine_within_one_ulp_of_exact_sum]),
     ("FP8 combine: scale of the wrong block",
      "scales[(size_t)r * nb + j / 128]", "scales[(size_t)r * nb + j % nb]",
-     [pins.test_combine_fp8_single_pair_matches_torch_dequant]),
+     [pins.test_combine_fp8_single_pair_matches_torch_dequant, pins.test_layout_worked_example]),
     ("dispatch backward: running sum dropped",
      "acc = acc + oracle_bf16_to_f32(grad_recv[(size_t)r * H + j]);",
      "acc = oracle_bf16_to_f32(grad_recv[(size_t)r * H + j]);",

@@ -268,6 +268,12 @@ def test_layout_worked_example():
     gy, gw = oracle.combine_backward(go, yb, slot, np.array(cb["weights"], np.float32), 9)
     assert np.array_equal(_f32(gy), np.array(bw["grad_y"], np.float32))
     assert np.array_equal(gw, np.array(bw["grad_w"], np.float32))
+    c8 = g["combine_fp8"]
+    q = np.repeat(np.array([int(c, 16) for c in c8["row_codes"]], np.uint8)[:, None], 256, axis=1)
+    sc = np.tile(np.array(c8["scales"], np.float32), (9, 1))
+    for wts, key in ((np.array(cb["weights"], np.float32), "out_weighted"), (None, "out_unit")):
+        o = _f32(oracle.combine_fp8(q, sc, slot, wts))
+        assert np.array_equal(o, np.repeat(np.array(c8[key], np.float32), 128, axis=1)), key
 
 
 
