@@ -700,3 +700,95 @@ def test_debug_launch_trace():
     kernels = [l.split()[1] for l in lines]
     assert kernels[:4] == ["layout_chunk_kernel", "scan_kernel", "dispatch_fp8_kernel", "combine_kernel"], lines
     assert all("grid=(" in l and "block=(" in l and "lds=" in l for l in lines)
+
+
+def test_hand_worked_examples_on_the_gpu(ep):
+    """The hand-worked examples in tests/golden/ (layout, slots, combine,
+    aligned and static layouts, both backward calls, the FP8 combine and the
+    expert-parallel flow) straight on the HIP path, with no oracle between:
+    every value is the one worked out by hand."""
+    import json
+    import os
+    dev = _dev()
+    gdir = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    g = json.load(open(os.path.join(gdir, "layout_worked_example.json")))
+    T, K, E, P, H = g["T"], g["K"], g["E"], g["P"], 8
+    t_idx = torch.tensor(g["topk_idx"], dtype=torch.int64, device=dev)
+    w = torch.tensor(g["combine"]["weights"], dtype=torch.float32, device=dev)
+    f32 = lambda t: workloads.f32_from_bf16_bits(_bits(t))
+
+    lay = ep.get_dispatch_layout(t_idx, E, P)
+    assert lay.num_tokens_per_expert.tolist() == g["num_tokens_per_expert"]
+    assert lay.num_tokens_per_partition.tolist() == g["num_tokens_per_partition"]
+    assert lay.is_token_in_partition.tolist() == g["is_token_in_partition"]
+    assert int(lay.num_invalid[0]) == g["num_invalid"]
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
+    _, _, h = ep.dispatch(x, w, lay, False, capacity_rows=15)
+    assert h.slot.tolist() == g["slot"]
+    assert h.expert_offset.tolist() == g["expert_offset"]
+    assert h.src_token.tolist()[:9] == g["src_token"]
+    # y[r] = [r, -r] repeated over the 8 channels
+    y = torch.tensor([[r, -r] * 4 for r in range(15)], dtype=torch.float32, device=dev).to(torch.bfloat16)
+    out = f32(ep.combine(y, h))
+    assert np.array_equal(out[:, :2], np.array(g["combine"]["out"], np.float32))
+    assert np.array_equal(out[:, 2:], np.tile(out[:, :2], (1, 3)))
+    # both backward calls (grad_out[t] = [1, 2] repeated)
+    bw = g["backward"]
+    gx = f32(ep.dispatch_backward(y, h))
+    assert np.array_equal(gx[:, :2], np.array(bw["dispatch_backward"], np.float32))
+    go = torch.tensor([[1.0, 2.0] * 4] * T, dtype=torch.float32, device=dev).to(torch.bfloat16)
+    gy, gw = ep.combine_backward(go, h, y=y)
+    assert np.array_equal(f32(gy)[:9, :2], np.array(bw["grad_y"], np.float32))
+    assert np.array_equal(gw.cpu().numpy(), 4 * np.array(bw["grad_w"], np.float32))   # 4 channel pairs
+    # capacity 6: drops and overflow
+    lay6 = ep.get_dispatch_layout(t_idx, E, P)
+    _, _, h6 = ep.dispatch(x, w, lay6, False, capacity_rows=6)
+    assert h6.slot.tolist() == g["capacity_6"]["slot"]
+    assert ep.handle_recv_counts(h6)[2] == ep.EP_ECAPACITY
+    # aligned layout, A = 2
+    lay2 = ep.get_dispatch_layout(t_idx, E, P, expert_alignment=2)
+    _, _, h2 = ep.dispatch(x, w, lay2, False)
+    assert h2.expert_offset.tolist() == g["aligned_2"]["expert_offset"]
+    assert h2.slot.tolist() == g["aligned_2"]["slot"]
+    # static low-latency layout, 2 rows per expert
+    _, _, lls = ep.low_latency_dispatch(x, t_idx, w, E, P, 2, False)
+    assert lls.handle.slot.tolist() == g["static_cap_2"]["slot"]
+    assert ep.handle_recv_counts(lls.handle)[2] == ep.EP_ECAPACITY
+    # FP8 combine: two blocks, scales 0.5 and 0.25
+    c8 = g["combine_fp8"]
+    codes = torch.tensor([int(c, 16) for c in c8["row_codes"]], dtype=torch.uint8, device=dev)
+    q = codes[:, None].repeat(1, 256)
+    q = torch.cat([q, torch.zeros((6, 256), dtype=torch.uint8, device=dev)])        # 15 rows
+    sc = torch.tensor(c8["scales"], dtype=torch.float32, device=dev).repeat(15, 1)
+    lay8 = ep.get_dispatch_layout(t_idx, E, P)
+    _, _, h8 = ep.dispatch(torch.zeros((T, 256), dtype=torch.bfloat16, device=dev), w, lay8, True,
+                           capacity_rows=15)
+    assert h8.slot.tolist() == g["slot"]
+    for wts, key in ((w, "out_weighted"), (None, "out_unit")):
+        o = f32(ep.combine_fp8(q, sc, h8, wts) if wts is not None else ep.dispatch_backward_fp8(q, sc, h8))
+        want = np.repeat(np.array(c8[key], np.float32), 128, axis=1)
+        assert np.array_equal(o, want), key
+
+    # the expert-parallel flow on its own worked example
+    ge = json.load(open(os.path.join(gdir, "ep_worked_example.json")))
+    we = torch.tensor(ge["topk_weights"], dtype=torch.float32, device=dev)
+    send_x, _, li, lw, play, part = ep.pack_for_ranks(x, t_idx, we, E, P, use_fp8=False)
+    assert part.tolist() == ge["part_idx"]
+    assert play.handle.slot.tolist() == ge["pack_slot"]
+    rows = sum(ge["pack_rows_per_destination"])
+    assert li[:rows].tolist() == ge["local_idx"]
+    assert np.array_equal(lw[:rows].cpu().numpy(), np.array(ge["local_w"], np.float32))
+    off = np.concatenate([[0], np.cumsum(ge["pack_rows_per_destination"])])
+    partial = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    for p in range(P):
+        r0, r1 = int(off[p]), int(off[p + 1])
+        ul = ep.get_dispatch_layout(li[r0:r1], E // P, 1)
+        _, _, uh = ep.dispatch(send_x[r0:r1], lw[r0:r1], ul, False)
+        assert uh.slot.tolist() == ge["unpack_slot"][p], p
+        n = ge["expert_outputs"]["rows_per_destination"][p]
+        yp = torch.tensor([[10 * p + u + 1, -(10 * p + u + 1)] * 4 for u in range(n)],
+                          dtype=torch.float32, device=dev).to(torch.bfloat16)
+        ep.combine(yp, uh, out=partial[r0:r1])
+    assert np.array_equal(f32(partial)[:, :2], np.array(ge["partials"], np.float32))
+    out_ep = f32(ep.dispatch_backward(partial, play.handle))
+    assert np.array_equal(out_ep[:, :2], np.array(ge["out"], np.float32))
