@@ -31,6 +31,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dispatch & combine logical GB/s on 1 MI355X (8192×7168 top-8); % HBM peak"
 HBM_PEAK_GBPS = 8000.0
+# output size past which the library's combine runs the token-owner form
+# (its streaming-store threshold)
+COMBINE_OWNER_OUT_BYTES = 160 << 20
 
 DESCR = {
     "tiny": "tiny: T=128 H=256 E=16 top-2 P=4, softmax routing, BF16 dispatch",
@@ -108,6 +111,8 @@ def byte_counts(wl, N):
 KERNEL_SOURCES = {
     "combine_kernel": ["combine_get_dispatch_scan_amd/csrc/combine.hip",
                        "combine_get_dispatch_scan_amd/csrc/device.h"],
+    "combine_owner_kernel": ["combine_get_dispatch_scan_amd/csrc/combine.hip",
+                             "combine_get_dispatch_scan_amd/csrc/device.h"],
     "dispatch_fp8_kernel": ["combine_get_dispatch_scan_amd/csrc/dispatch.hip",
                             "combine_get_dispatch_scan_amd/csrc/dispatch_rows.h",
                             "combine_get_dispatch_scan_amd/csrc/device.h"],
@@ -380,7 +385,7 @@ def event_stride(steps):
     return max(1, steps // 20)
 
 
-def cold_record(bc, logical, step_us, disp_us, comb_us, disp_kernel):
+def cold_record(bc, logical, step_us, disp_us, comb_us, disp_kernel, comb_kernel="combine_kernel"):
     """Cold-cache figures: every measured step or call runs right after a
     2 GiB read that evicts the Infinity Cache and the L2s; medians of 10."""
     med = lambda v: v[len(v) // 2]
@@ -394,7 +399,7 @@ def cold_record(bc, logical, step_us, disp_us, comb_us, disp_kernel):
             "dispatch": {"kernel": disp_kernel,
                          "us": round(med(disp_us), 2), "bytes_per_launch": bc["dispatch_alg"],
                          "frac": frac(bc["dispatch_alg"], med(disp_us))},
-            "combine": {"kernel": "combine_kernel", "us": round(med(comb_us), 2),
+            "combine": {"kernel": comb_kernel, "us": round(med(comb_us), 2),
                         "bytes_per_launch": bc["combine_alg"], "frac": frac(bc["combine_alg"], med(comb_us))},
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "bound": "hbm",
         },
@@ -790,8 +795,11 @@ def main():
     bc = byte_counts(wl, N)
     dom_bytes = bc["dispatch_alg"] if dom == "dispatch" else bc["combine_alg"]
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+    # the combine form the launcher picks: the token-owner kernel for outputs
+    # past 160 MiB (streaming stores), the segmented kernel below
+    combine_name = "combine_owner_kernel" if T * H * 2 > COMBINE_OWNER_OUT_BYTES else "combine_kernel"
     dom_kernel = {"dispatch": "dispatch_fp8_kernel" if wl.use_fp8 else "dispatch_bf16_kernel",
-                  "combine": "combine_kernel"}[dom]
+                  "combine": combine_name}[dom]
 
     # practical ceilings on this GPU, same run: a plain 1 GiB device copy and fill
     def rate(fn, nbytes, reps=10):
@@ -928,7 +936,7 @@ def main():
         "value_protocol": "warm: the K timed steps run back to back on resident inputs, caches not "
                           "flushed (one step touches about 1.6 GB against the 256 MB Infinity Cache)",
         "cold": cold_record(bc, logical, cold_us, cold_disp_us, cold_comb_us,
-                            "dispatch_fp8_kernel" if wl.use_fp8 else "dispatch_bf16_kernel"),
+                            "dispatch_fp8_kernel" if wl.use_fp8 else "dispatch_bf16_kernel", combine_name),
         "step_us": step_stats,
         "phases_us": {k: round(v * 1e3, 2) for k, v in phases.items()},
         "ceilings_GBps": {"torch_copy_1GiB": round(copy_gbps, 1), "torch_fill_1GiB": round(fill_gbps, 1)},

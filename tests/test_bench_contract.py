@@ -158,3 +158,18 @@ def test_oracle_timings_beside_the_side_figures(name):
         assert set(side) == {"backward"}
     assert all(v >= 0 for d in side.values() for v in d.values())
     assert bench.cpu_decode_figure() > 0
+
+
+def test_the_roofline_names_the_combine_form_the_launcher_picks():
+    """bench.py names the dominant combine by the library's own rule: outputs
+    past the streaming-store threshold run the token-owner form (the large
+    workload), smaller ones the segmented form (V3); the threshold is the one
+    combine.hip compiles with."""
+    import re
+    src = open(os.path.join(ROOT, "combine_get_dispatch_scan_amd", "csrc", "combine.hip")).read()
+    m = re.search(r"#define EP_COMBINE_STREAM_OUT_BYTES \((\d+)ll << (\d+)\)", src)
+    assert m, "threshold define not found"
+    assert bench.COMBINE_OWNER_OUT_BYTES == int(m.group(1)) << int(m.group(2))
+    v3, large = workloads.config("v3"), workloads.config("large")
+    assert v3.T * v3.H * 2 <= bench.COMBINE_OWNER_OUT_BYTES < large.T * large.H * 2
+    assert "combine_owner_kernel" in bench.KERNEL_SOURCES
