@@ -111,11 +111,21 @@ _SIGS = {
 
 
 def load():
-    """Load libmoe_ep.so (raises if it has not been built)."""
+    """Load libmoe_ep.so (raises if it has not been built).
+
+    torch, when installed, is imported first: its HIP libraries load the HIP
+    runtime torch ships, and the library then binds to that same runtime (it
+    asks for the runtime by its soname).  Loaded the other way round, torch
+    would load a second HIP runtime into the process, and the two do not
+    share the device."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, (args, res) in _SIGS.items():
             f = getattr(L, name)

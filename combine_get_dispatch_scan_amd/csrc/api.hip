@@ -599,7 +599,8 @@ int ep_combine(const void* y, const ep_handle_t* handle, const float* topk_weigh
     if (T > 0 && (!out || !aligned(out, 16)))
         return fail(EP_EINVAL, "out must be a non-NULL 16-byte aligned device pointer");
     if (T > 0 && handle->capacity_rows > 0 && (!y || !aligned(y, 16)))
-        return fail(EP_EINVAL, "y must be a non-NULL 16-byte aligned device pointer");
+        return fail(EP_EINVAL, "y must be a non-NULL 16-byte aligned device pointer (a receive-row buffer, "
+                    "also when no pair was dispatched)");
     hipError_t e = moe_ep::launch_combine(y, T, handle->hidden, handle->num_topk, handle->slot, w,
                                           out, stream);
     if (e != hipSuccess)
@@ -618,7 +619,8 @@ int ep_dispatch_backward(const void* grad_recv, const ep_handle_t* handle, void*
     if (T > 0 && (!grad_x || !aligned(grad_x, 16)))
         return fail(EP_EINVAL, "grad_x must be a non-NULL 16-byte aligned device pointer");
     if (T > 0 && handle->capacity_rows > 0 && (!grad_recv || !aligned(grad_recv, 16)))
-        return fail(EP_EINVAL, "grad_recv must be a non-NULL 16-byte aligned device pointer");
+        return fail(EP_EINVAL, "grad_recv must be a non-NULL 16-byte aligned device pointer (a receive-row "
+                    "buffer, also when no pair was dispatched)");
     hipError_t e = moe_ep::launch_combine(grad_recv, T, handle->hidden, handle->num_topk,
                                           handle->slot, nullptr, grad_x, stream);
     if (e != hipSuccess)

@@ -317,7 +317,9 @@ int ep_dispatch_cached(const void* x, const ep_handle_t* handle,
  * with no dispatched pair gets a +0 row (GeekNews usage section: combine
  * reduces expert outputs back to their origin; stakiran section 3).
  *
- *   y             device bf16 [rows*H], rows in the receive order of dispatch
+ *   y             device bf16 [rows*H], rows in the receive order of dispatch;
+ *                 non-NULL whenever capacity_rows > 0, even if no pair was
+ *                 dispatched (the host does not know N without a sync)
  *   handle        a dispatched handle
  *   topk_weights  device fp32 [T*K], or NULL to use the copy dispatch took
  *   out           device bf16 [T*H]

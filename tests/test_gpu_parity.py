@@ -76,7 +76,9 @@ def run_gpu(ep, idx, w, x, y, E, P, use_fp8, capacity=None, guard_rows=3, pass_w
         recv_full=recv_full.cpu().numpy(), sc_full=None if sc_full is None else sc_full.cpu().numpy(),
     )
     if y is not None:
-        t_y = _bf16_tensor(y, dev) if y.shape[0] > 0 else torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+        # a receive-row buffer even when no pair was dispatched (the library
+        # needs one whenever the capacity is not 0)
+        t_y = _bf16_tensor(y, dev) if y.shape[0] > 0 else torch.zeros((1, H), dtype=torch.bfloat16, device=dev)
         cw = None if combine_weights is None else torch.from_numpy(combine_weights).to(dev)
         out = torch.full((T, H), 0x7777, dtype=torch.int16, device=dev).view(torch.bfloat16)
         ep.combine(t_y, h, topk_weights=cw, out=out)
@@ -792,3 +794,44 @@ def test_hand_worked_examples_on_the_gpu(ep):
     assert np.array_equal(f32(partial)[:, :2], np.array(ge["partials"], np.float32))
     out_ep = f32(ep.dispatch_backward(partial, play.handle))
     assert np.array_equal(out_ep[:, :2], np.array(ge["out"], np.float32))
+
+
+def test_nothing_dispatched_still_needs_a_row_buffer(ep):
+    """Every id masked: N = 0 rows, capacity T*K.  combine gives +0 rows from
+    a receive buffer of any size; an empty (NULL) buffer is refused with a
+    message, since the host cannot know N without a sync."""
+    dev = _dev()
+    T, K, E, P, H = 3, 2, 8, 2, 64
+    t_idx = torch.full((T, K), -1, dtype=torch.int64, device=dev)
+    lay = ep.get_dispatch_layout(t_idx, E, P)
+    x = torch.randn((T, H), device=dev).to(torch.bfloat16)
+    _, _, h = ep.dispatch(x, torch.ones((T, K), device=dev), lay, False)
+    assert ep.handle_recv_counts(h)[1] == 0
+    out = ep.combine(torch.zeros((1, H), dtype=torch.bfloat16, device=dev), h)
+    torch.cuda.synchronize()
+    assert not _bits(out).any()
+    with pytest.raises(ep.EpError, match="also when no pair was dispatched"):
+        ep.combine(torch.empty((0, H), dtype=torch.bfloat16, device=dev), h)
+
+
+def test_library_loaded_before_torch():
+    """Loading the library before the caller imports torch still gives one
+    HIP runtime (load() imports torch first): a small forward in a child
+    process that does exactly that."""
+    import os
+    import subprocess
+    import sys
+    _dev()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import combine_get_dispatch_scan_amd as ep\n"
+        "ep.load()\n"
+        "import torch\n"
+        "d = torch.device('cuda:0')\n"
+        "lay = ep.get_dispatch_layout(torch.randint(0, 16, (40, 2), device=d), 16, 4)\n"
+        "recv, sc, h = ep.dispatch(torch.ones((40, 128), device=d).to(torch.bfloat16), None, lay, True)\n"
+        "print('N', ep.handle_recv_counts(h)[1])\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "N " in r.stdout
