@@ -127,3 +127,75 @@ def test_rank_flow_random(ep, case):
         assert np.array_equal(g["rows"], u["recv_x"][:u["rows"]]), p
     assert np.array_equal(partials, ref["partials"])
     assert np.array_equal(out, ref["out"])
+
+
+def _bits16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("seed", [5, 6, 7])
+def test_call_sequences_on_one_handle(ep, seed):
+    """Random sequences of calls on one handle, each step against the oracle:
+    re-dispatch with changing capacity (0, N - 1, N, T*K, any) and payload
+    mode, cached dispatch of new rows, combine, dispatch backward, and the
+    asynchronous count readback.  The overflow status always belongs to the
+    latest dispatch."""
+    dev = ll._dev()
+    bf = lambda b: ll._bf16(b, dev)
+    rng = np.random.default_rng(seed)
+    for case in range(10):
+        P = int(rng.choice([1, 2, 4, 8, 16]))
+        E = P * int(rng.integers(1, 256 // P + 1))
+        K = int(rng.integers(1, 9))
+        T = int(rng.integers(1, 1500))
+        H = 128 * int(rng.integers(1, 9))
+        idx, w = _ids(int(rng.integers(1 << 30)), T, E, K, bool(rng.integers(0, 2)))
+        print(f"[random] sequence seed={seed} case={case} T={T} H={H} E={E} K={K} P={P}", flush=True)
+        t_idx, t_w = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
+        lay = ep.get_dispatch_layout(t_idx, E, P)
+        h = lay.handle
+        N = oracle.run_all(idx, w, None, E, P, False)["N"]
+        host_buf = torch.empty(E + 5, dtype=torch.int32, pin_memory=True)
+        cur = None
+        for step in range(int(rng.integers(3, 8))):
+            op = "dispatch" if cur is None else str(rng.choice(
+                ["dispatch", "dispatch", "cached", "combine", "backward", "counts_async"]))
+            if op == "dispatch":
+                fp8 = bool(rng.integers(0, 2))
+                cap = int(rng.choice([T * K, N, max(0, N - 1), int(rng.integers(0, N + 1)), 0]))
+                x = workloads.random_rows(int(rng.integers(1 << 30)), T, H, "normal")
+                recv, sc, _ = ep.dispatch(bf(x), t_w, lay, fp8, capacity_rows=cap)
+                ref = oracle.run_all(idx, w, x, E, P, fp8, capacity=cap)
+                assert np.array_equal(h.slot.cpu().numpy(), ref["slot"])
+                rows = ref["rows"]
+                got = recv.view(torch.uint8).cpu().numpy() if fp8 else _bits16(recv)
+                assert np.array_equal(got[:rows], ref["recv_x"])
+                if fp8:
+                    assert np.array_equal(sc[:rows].cpu().numpy().view(np.uint32), ref["recv_scales"].view(np.uint32))
+                _, n, st = ep.handle_recv_counts(h)
+                cur = (fp8, cap, ref)
+            else:
+                fp8, cap, ref = cur
+                if op == "cached":
+                    x2 = workloads.random_rows(int(rng.integers(1 << 30)), T, H, "normal")
+                    r2, _ = ep.dispatch_cached(bf(x2), h)
+                    ref2 = oracle.run_all(idx, w, x2, E, P, fp8, capacity=cap)
+                    got = r2.view(torch.uint8).cpu().numpy() if fp8 else _bits16(r2)
+                    assert np.array_equal(got[:ref2["rows"]], ref2["recv_x"])
+                elif op == "combine":
+                    y = workloads.random_rows(int(rng.integers(1 << 30)), max(cap, 1), H, "normal")
+                    assert np.array_equal(_bits16(ep.combine(bf(y), h)),
+                                          oracle.combine(y[:ref["rows"]], ref["slot"], w))
+                elif op == "backward":
+                    gr = workloads.random_rows(int(rng.integers(1 << 30)), max(cap, 1), H, "normal")
+                    assert np.array_equal(_bits16(ep.dispatch_backward(bf(gr), h)),
+                                          oracle.dispatch_backward(gr[:ref["rows"]], ref["slot"]))
+                else:
+                    ev = torch.cuda.Event()
+                    ep.handle_recv_counts_async(h, host_buf)
+                    ev.record()
+                    ev.synchronize()
+                    _, n, st = ep.recv_counts_decode(h, host_buf)
+            if op in ("dispatch", "counts_async"):
+                want = ep.EP_ECAPACITY if cur[2]["overflow"] else (ep.EP_EIDS if cur[2]["num_invalid"] else ep.EP_OK)
+                assert st == want and n == N, (op, st, want)
