@@ -835,3 +835,90 @@ def test_library_loaded_before_torch():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert "N " in r.stdout
+
+
+@pytest.mark.parametrize("T,H,K,E,P,fp8,dirty", [(1, 128, 1, 1, 1, False, False),
+                                                 (3000, 512, 16, 1024, 64, True, True),
+                                                 (257, 256, 8, 32, 4, False, True),
+                                                 (1500, 2048, 8, 256, 8, True, False)])
+def test_graph_capture_of_every_call(ep, T, H, K, E, P, fp8, dirty):
+    """layout, dispatch, the asynchronous count readback (a copy node),
+    combine and both backward calls captured once in one HIP graph, then
+    replayed on three new batches with eager work between the replays; every
+    replay against the oracle."""
+    dev = _dev()
+    cap = T * K
+    s_idx = torch.empty((T, K), dtype=torch.int64, device=dev)
+    s_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    s_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    s_y = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    s_g = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ep.ep_workspace_bytes(T, K, E, P), dtype=torch.uint8, device=dev)
+    ntpp = torch.empty(P, dtype=torch.int32, device=dev)
+    ntpe = torch.empty(E, dtype=torch.int32, device=dev)
+    itip = torch.empty((T, P), dtype=torch.uint8, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    recv = torch.empty((cap, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    sc = torch.empty((cap, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    gx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    gy = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    gw = torch.empty((T, K), dtype=torch.float32, device=dev)
+    host = torch.empty(E + 5, dtype=torch.int32, pin_memory=True)
+    h = ep.ep_handle_t()
+    p = lambda t: None if t is None else t.data_ptr()
+
+    def step():
+        s = ep._stream()
+        assert ep.ep_get_dispatch_layout(p(s_idx), T, K, E, P, p(ntpp), p(ntpe), p(itip), p(ninv),
+                                         p(ws), ws.numel(), h, s) == ep.EP_OK
+        assert ep.ep_dispatch(p(s_x), p(s_w), H, int(fp8), p(recv), p(sc), cap, h, s) == ep.EP_OK
+        assert ep.ep_handle_recv_counts_async(h, host.data_ptr(), s) == ep.EP_OK
+        assert ep.ep_combine(p(s_y), h, None, p(out), s) == ep.EP_OK
+        assert ep.ep_dispatch_backward(p(s_y), h, p(gx), s) == ep.EP_OK
+        assert ep.ep_combine_backward(p(s_g), p(s_y), h, None, p(gy), p(gw), s) == ep.EP_OK
+
+    kw = dict(distinct=K <= E and not dirty)
+    if dirty:
+        kw.update(mask_frac=0.1, invalid_frac=0.03, dup_frac=0.05)
+    cases = []
+    for r in range(4):
+        idx, w = workloads.random_case(700 + 10 * r + T % 7, T, E, K, **kw)
+        cases.append((idx, w, workloads.random_rows(710 + r, T, H, "normal"),
+                      workloads.random_rows(720 + r, cap, H, "normal"),
+                      workloads.random_rows(730 + r, T, H, "normal")))
+
+    def load(c):
+        s_idx.copy_(torch.from_numpy(c[0]))
+        s_w.copy_(torch.from_numpy(c[1]))
+        s_x.copy_(_bf16_tensor(c[2], dev))
+        s_y.copy_(_bf16_tensor(c[3], dev))
+        s_g.copy_(_bf16_tensor(c[4], dev))
+
+    load(cases[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                        # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for c in cases[1:]:
+        load(c)
+        junk = torch.randn(1 << 20, device=dev).sum()     # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        idx, w, x, y, go = c
+        ref = oracle.run_all(idx, w, x, E, P, fp8)
+        rows = ref["rows"]
+        assert np.array_equal(np.diff(host.numpy()[:E + 1]), ref["num_tokens_per_expert"])
+        assert np.array_equal(ntpe.cpu().numpy(), ref["num_tokens_per_expert"])
+        got = recv.view(torch.uint8).cpu().numpy() if fp8 else _bits(recv)
+        assert np.array_equal(got[:rows], ref["recv_x"])
+        assert np.array_equal(_bits(out), oracle.combine(y[:rows], ref["slot"], w))
+        assert np.array_equal(_bits(gx), oracle.dispatch_backward(y[:rows], ref["slot"]))
+        ref_gy, _ = oracle.combine_backward(go, y[:rows], ref["slot"], w, cap)
+        assert np.array_equal(_bits(gy)[:rows], ref_gy[:rows])
+        del junk
