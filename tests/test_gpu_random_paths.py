@@ -83,6 +83,7 @@ def test_aligned_layout_random(ep, case):
     if fp8_input:
         rng = np.random.default_rng(9500 + i)
         xq = rng.integers(0, 256, (T, H), dtype=np.uint32).astype(np.uint8)
+        xq[(xq & 0x7F) == 0x7F] ^= 1                   # finite codes only (NaN is outside the contract)
         xs = rng.standard_normal((T, H // 128)).astype(np.float32)
         lay, h, recv, sc, cap, _, _ = gl._run(ep, idx, w, xq, E, P, A, True, x_scales=xs,
                                               col_major=col_major)
@@ -99,6 +100,17 @@ def test_aligned_layout_random(ep, case):
     out = ep.combine(gl._bf16(y, gl._dev()), h)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(gl._bits(out), oracle.combine(y, ref["slot"], w))
+    if fp8:
+        # the FP8 rows and scales as dispatch wrote them (column-major when
+        # asked), through the FP8 combine and the FP8 dispatch backward
+        out8 = ep.combine_fp8(recv[:cap], sc, h)
+        gx8 = ep.dispatch_backward_fp8(recv[:cap], sc, h)
+        torch.cuda.synchronize()
+        rows = ref["rows"]
+        q = recv[:rows].cpu().numpy()
+        s_rm = (sc.cpu().numpy()[:, :rows].T if col_major else sc.cpu().numpy()[:rows])
+        np.testing.assert_array_equal(gl._bits(out8), oracle.combine_fp8(q, np.ascontiguousarray(s_rm), ref["slot"], w))
+        np.testing.assert_array_equal(gl._bits(gx8), oracle.combine_fp8(q, np.ascontiguousarray(s_rm), ref["slot"], None))
 
 
 def _ranks_cases(n=15, seed=13):
